@@ -1,0 +1,149 @@
+"""fp64 CPU oracle for scaled-dot-product attention (O and the per-row logsumexp L).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. It shares no code
+with the HIP path (``scaled_dot_product_12_amd``) and neither imports the
+other; both are fed by the seeded generators in
+``scaled_dot_product_12_amd.inputs``, which hold none of the method's
+arithmetic.
+
+What it computes is the plain definition, row by row, in IEEE fp64 (see
+``attn_oracle.c``): softmax(scale * Q K^T [+ top-left causal mask]) V and
+L = max + ln(sum exp(s - max)). Sources: "Extend Thunder with CUDA-Python",
+Python reference section (flash_attention_reference, whose tiled loop reduces
+to this when one tile spans all keys, and whose causal mask keeps key <= query
+in absolute positions); "Blackwell Attention Example", attention kernel (lse as
+one value per query row, [B, H, M]).
+
+Inputs are widened to fp64 exactly (fp32 and bf16 values are representable),
+so for bf16 the oracle sees the bf16-rounded values the GPU sees.
+
+Parity pins (tests/test_oracle_pins.py): a 50-digit ``decimal`` brute force,
+an independent fp64 re-implementation of the pages' tiled online algorithm,
+torch's fp64 CPU SDPA, and closed forms / invariants. Every function here is
+pinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Iterable, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_attn.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.oracle_attn_fwd.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                        i64, ctypes.c_double, ctypes.c_int,
+                                        ctypes.c_int]
+        lib.oracle_attn_fwd.restype = ctypes.c_int
+        lib.oracle_attn_rows.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                         i64, ctypes.c_double, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int64), i64,
+                                         ctypes.c_int]
+        lib.oracle_attn_rows.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def host_threads() -> int:
+    """Threads the oracle uses by default: every core this process may run on."""
+    return len(os.sched_getaffinity(0))
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening of an fp32 / bf16 / fp64 array (numpy or torch) to fp64."""
+    if hasattr(x, "detach"):  # torch tensor, possibly bf16 which numpy lacks
+        import torch
+        x = x.detach().to(device="cpu", dtype=torch.float64).contiguous().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D), the scale the pages use when none is given (fp64)."""
+    return 1.0 / math.sqrt(D)
+
+
+def _shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("oracle expects [B,H,M,D] / [B,H,N,D] arrays")
+    B, H, M, D = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    return B, H, M, k.shape[2], D
+
+
+def attn_fwd(q, k, v, is_causal: bool = False, scale: float | None = None,
+             nthreads: int | None = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Every row: returns (O [B,H,M,D], L [B,H,M]) as fp64 numpy arrays."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, M, N, D = _shapes(q, k, v)
+    if scale is None:
+        scale = default_scale(D)
+    o = np.empty((B, H, M, D), dtype=np.float64)
+    lse = np.empty((B, H, M), dtype=np.float64)
+    rc = _load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 B, H, M, N, D, float(scale), int(bool(is_causal)),
+                                 nthreads or host_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_attn_fwd failed with {rc}")
+    return o, lse
+
+
+def attn_rows(q, k, v, rows: Iterable[Tuple[int, int, int]],
+              is_causal: bool = False, scale: float | None = None,
+              nthreads: int | None = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Selected query rows (b, h, i): returns (O [n, D], L [n]) in fp64.
+
+    Only the heads that the rows touch are widened, so this stays cheap on
+    inputs far larger than the full oracle could finish.
+    """
+    rows = [tuple(int(t) for t in r) for r in rows]
+    if q.ndim != 4:
+        raise ValueError("oracle expects [B,H,M,D] arrays")
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    if scale is None:
+        scale = default_scale(D)
+    out_o = np.empty((len(rows), D), dtype=np.float64)
+    out_l = np.empty((len(rows),), dtype=np.float64)
+    by_head = {}
+    for t, (b, h, i) in enumerate(rows):
+        if not (0 <= b < B and 0 <= h < H and 0 <= i < M):
+            raise ValueError(f"row {(b, h, i)} out of range")
+        by_head.setdefault((b, h), []).append((t, i))
+    lib = _load()
+    for (b, h), items in by_head.items():
+        qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+        if kh.shape != (N, D) or vh.shape != (N, D):
+            raise ValueError("k / v head shape mismatch")
+        ids = np.array([i for _, i in items], dtype=np.int64)
+        o = np.empty((len(items), D), dtype=np.float64)
+        lse = np.empty((len(items),), dtype=np.float64)
+        rc = lib.oracle_attn_rows(_ptr(qh), _ptr(kh), _ptr(vh), _ptr(o), _ptr(lse),
+                                  1, 1, M, N, D, float(scale), int(bool(is_causal)),
+                                  ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                  len(items), nthreads or host_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_attn_rows failed with {rc}")
+        for n, (t, _) in enumerate(items):
+            out_o[t] = o[n]
+            out_l[t] = lse[n]
+    return out_o, out_l
