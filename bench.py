@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward (libmi355_attn) on one MI355X.
+
+One step = one attn_fwd call over the headline workload: bf16 B=4, H=16,
+M=N=4096, D=128, non-causal (the long-sequence configuration whose MFMA
+roofline target is stated; the pages' own bench shapes are bf16 long-context
+tensors of this kind). Inputs are seeded synthetic N(0,1) draws rounded to
+bf16, resident in HBM before timing starts; outputs are preallocated.
+
+Prints ONE JSON line with the metric (TFLOP/s with 4*B*H*M*N*D FLOPs, halved
+when causal), the roofline of the dominant kernel, the CPU oracle's rate on a
+bounded sample of the same workload, and the other workloads (fp32 single
+head, fp32 batch-96 non-causal / causal, the two axial passes, bf16 causal
+8192) as additional measurements.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+                       [--no-cpu-baseline] [--workload c4]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks.
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # fp32 (vector and MFMA)
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_dot_product_12_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this workload or the kernels have changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, graph=False):
+    """Average GPU time per call (ms) with HIP events on the launch stream.
+    graph=True captures the calls in one HIP graph first (for microsecond
+    kernels whose Python launch cost would otherwise leave the GPU idle)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(steps):
+                    fn()
+        torch.cuda.synchronize()
+        g.replay()  # warm the graph
+        torch.cuda.synchronize()
+        run = g.replay
+    else:
+        def run():
+            for _ in range(steps):
+                fn()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def gpu_setup(w):
+    import torch
+    import scaled_dot_product_12_amd as attn
+    from scaled_dot_product_12_amd.inputs import workload_inputs
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def fn():
+        attn.attn_fwd(q, k, v, is_causal=w.causal, scale=w.scale, out=(o, lse))
+    return fn, (q, k, v, o, lse)
+
+
+def spot_parity(w, tensors, n=48):
+    """Max |dO|, |dL| of the last timed call on n sampled rows vs the oracle."""
+    import torch
+    import oracle
+    from scaled_dot_product_12_amd.inputs import workload_inputs
+    q, k, v = workload_inputs(w)
+    o, lse = tensors[3], tensors[4]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(123)
+    B, H, M, _ = q.shape
+    rows = sorted({(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(M)))
+                   for _ in range(n)} | {(0, 0, 0), (B - 1, H - 1, M - 1)})
+    ro, rl = oracle.attn_rows(q, k, v, rows, is_causal=w.causal, scale=w.scale)
+    go = np.stack([o[b, h, i].float().cpu().double().numpy() for b, h, i in rows])
+    gl = np.array([float(lse[b, h, i]) for b, h, i in rows])
+    return float(np.abs(go - ro).max()), float(np.abs(gl - rl).max()), len(rows)
+
+
+def cpu_baseline(w, target_s):
+    """The oracle as it is, on the host cores, over a bounded row sample of
+    the same workload; rate scaled to TFLOP/s with the same FLOP count per
+    row (4*N_visible*D)."""
+    import oracle
+    from scaled_dot_product_12_amd.inputs import workload_inputs
+    q, k, v = workload_inputs(w)
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    rng = np.random.default_rng(7)
+    cores = oracle.host_threads()
+
+    def sample(n):
+        heads = [(b, h) for b in range(B) for h in range(H)]
+        rng.shuffle(heads)
+        rows, per = [], max(1, min(M, n // min(len(heads), 4) + 1))
+        for b, h in heads[:4]:
+            for i in np.linspace(0, M - 1, per).astype(int):
+                rows.append((b, h, int(i)))
+        return rows[:n]
+
+    def flops(rows):
+        return sum(4.0 * (min(i + 1, N) if w.causal else N) * D for _, _, i in rows)
+
+    n = max(cores * 4, 64)
+    rows = sample(n)
+    t0 = time.perf_counter()
+    oracle.attn_rows(q, k, v, rows, is_causal=w.causal, scale=w.scale, nthreads=cores)
+    dt = time.perf_counter() - t0
+    rate = flops(rows) / max(dt, 1e-9)
+    # second, sized run: about target_s of work
+    n2 = int(min(B * H * M, max(n, target_s * rate / (4.0 * N * D))))
+    rows = sample(n2)
+    t0 = time.perf_counter()
+    oracle.attn_rows(q, k, v, rows, is_causal=w.causal, scale=w.scale, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops(rows) / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} query rows of {w.describe()} (4 heads, evenly spaced "
+                      f"rows), fp64, {dt:.1f} s wall"}
+
+
+def measure(w, steps, warmup, graph):
+    fn, tensors = gpu_setup(w)
+    ms, wall = time_launches(fn, steps, warmup, graph=graph)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    gbs = w.algorithmic_bytes() / (ms * 1e-3) / 1e9
+    return ms, wall, tflops, gbs, tensors
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the attention "
+              "forward here has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import __graft_entry__ as ge
+    from scaled_dot_product_12_amd.inputs import WORKLOADS
+    ge.ensure_built()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = WORKLOADS[a.workload]
+    print(f"[bench] headline {w.describe()}", file=sys.stderr, flush=True)
+    ms, wall, tflops, gbs, tensors = measure(w, a.steps, a.warmup, graph=False)
+    do, dl, nrows = spot_parity(w, tensors)
+    del tensors
+    torch.cuda.empty_cache()
+    print(f"[bench] {ms*1e3:.1f} us/step {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    is_bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_FP32_TFLOPS
+    traffic = stored_traffic(w.name)
+
+    extra = {}
+    if not a.no_extra:
+        for name in ("c1", "c2", "c2c", "c3r", "c3c", "c5"):
+            if name == w.name:
+                continue
+            x = WORKLOADS[name]
+            small = x.flops < 1e9
+            steps = 200 if small else max(5, min(50, int(2e12 / x.flops)))
+            print(f"[bench] extra {x.describe()}", file=sys.stderr, flush=True)
+            xms, _, xtf, xgbs, xt = measure(x, steps, 3, graph=small)
+            xdo, xdl, _ = spot_parity(x, xt, n=16)
+            del xt
+            torch.cuda.empty_cache()
+            xpeak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_FP32_TFLOPS
+            extra[name] = {
+                "workload": x.describe(), "us_per_call": round(xms * 1e3, 3),
+                "tflops": round(xtf, 3), "frac_compute_peak": round(xtf / xpeak, 4),
+                "gbs": round(xgbs, 1), "frac_hbm_peak": round(xgbs / PEAK_HBM_GBS, 4),
+                "timing": "HIP graph of %d calls" % steps if small else "%d calls" % steps,
+                "spot_max_abs_dO": xdo, "spot_max_abs_dL": xdl,
+            }
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, a.cpu_seconds)
+
+    line = {
+        "metric": "attention fwd TFLOP/s on 1 MI355X (4*B*H*M*N*D)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if is_bf16 else "fp32",
+        "data": "synthetic (seeded N(0,1), rounded to bf16)" if is_bf16 else "synthetic (seeded N(0,1))",
+        "config": {"workload": w.describe(), "B": w.B, "H": w.H, "M": w.M, "N": w.N,
+                   "D": w.D, "causal": w.causal, "seed": w.seed,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "hbm_gbs_algorithmic": round(gbs, 1),
+        "wall_s_timed": round(wall, 4),
+        "spot_parity": {"rows": nrows, "max_abs_dO": do, "max_abs_dL": dl},
+        "workloads": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/*
+ * mi355_attn.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward.
+ *
+ * The operation (FlashAttention-2 forward, as stated by "Extend Thunder with
+ * CUDA-Python", Python reference section, and "Blackwell Attention Example",
+ * attention kernel): for every batch b, head h and query row i
+ *
+ *     s_j  = scale * <q[b,h,i,:], k[b,h,j,:]>      j = 0 .. N-1
+ *            (causal: only j <= i, top-left aligned, as the reference's mask
+ *             keeps key index <= query index in absolute positions)
+ *     O[b,h,i,:] = sum_j softmax(s)_j * v[b,h,j,:]
+ *     L[b,h,i]   = ln( sum_j exp(s_j) )            natural-log logsumexp
+ *
+ * computed tile by tile with a running max and running sum so that the
+ * M x N score matrix is never stored. L is what the Python reference returns
+ * as m + log(l); the Helion example returns the same quantity in base 2 and
+ * it is converted here to the natural log.
+ *
+ * Layout: contiguous row-major. q and o are [B, H, M, D]; k and v are
+ * [B, H, N, D]; lse is [B, H, M] fp32 (the reference's [.., M, 1] is the same
+ * memory). q, k, v and o share one element type (MI355_ATTN_FP32 or
+ * MI355_ATTN_BF16); lse is always fp32.
+ *
+ * Ownership: every pointer is caller-owned device memory on the current HIP
+ * device. The library allocates nothing, keeps no pointer after a call
+ * returns, and has no mutable global state.
+ *
+ * Execution: attn_fwd enqueues its kernel on `stream` (a hipStream_t; NULL is
+ * the null stream) and returns without synchronising. Faults inside the
+ * kernel surface at the caller's next synchronisation. Calls are reentrant.
+ *
+ * Errors: every argument check happens before any HIP call; a call that fails
+ * a check launches nothing and writes nothing.
+ */
+#ifndef MI355_ATTN_H
+#define MI355_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+#define MI355_ATTN_FP32 0
+#define MI355_ATTN_BF16 1
+
+/* Status codes. */
+#define MI355_ATTN_OK                0 /* success (also: nothing to do)            */
+#define MI355_ATTN_ERR_INVALID_ARG   1 /* bad pointer / size / flag / overlap      */
+#define MI355_ATTN_ERR_UNSUPPORTED   2 /* valid but not implemented (D, size)      */
+#define MI355_ATTN_ERR_MISALIGNED    3 /* q/k/v/o not 16-byte or lse not 4-byte    */
+#define MI355_ATTN_ERR_HIP           4 /* the HIP launch reported an error         */
+
+/* Kernel paths (attn_fwd_path / attn_fwd_select_path). */
+#define MI355_ATTN_PATH_AUTO  0 /* let the library choose                        */
+#define MI355_ATTN_PATH_MAIN  1 /* tiled MFMA kernel with the online softmax      */
+#define MI355_ATTN_PATH_SMALL 2 /* one-tile, LDS-resident kernel for short rows   */
+
+/*
+ * attn_fwd -- O and L of scaled-dot-product attention (see the top of this
+ * file for the definition and layouts).
+ *
+ *   q, k, v    device pointers to the inputs, element type `dtype`.
+ *   o          device pointer to the output [B,H,M,D], element type `dtype`.
+ *   lse        device pointer to the fp32 output [B,H,M] (natural log).
+ *   B, H       batch and head counts (>= 0).
+ *   M, N       query and key lengths (M >= 0; N >= 1 whenever B*H*M > 0).
+ *   D          head dimension: 16, 32, 64 or 128.
+ *   scale      multiplier of q.k, finite; the pages' default is 1/sqrt(D)
+ *              (the Python binding passes that when scale is None).
+ *   is_causal  0 or 1; 1 masks key j > query i (top-left aligned).
+ *   dtype      MI355_ATTN_FP32 or MI355_ATTN_BF16.
+ *   stream     hipStream_t to enqueue on (NULL: null stream).
+ *
+ * Returns MI355_ATTN_OK, or:
+ *   INVALID_ARG  a null pointer while B*H*M > 0; B, H or M < 0; N < 1 while
+ *                B*H*M > 0; D < 1; non-finite scale; is_causal not 0/1; bad
+ *                dtype; o or lse overlapping q, k, v or each other.
+ *   UNSUPPORTED  D not in {16, 32, 64, 128}; a size whose element count or
+ *                launch grid does not fit the kernels' index types.
+ *   MISALIGNED   q, k, v or o not 16-byte aligned, or lse not 4-byte aligned.
+ *   HIP_ERROR    the launch failed (hipGetLastError).
+ * B*H*M == 0 returns OK without launching.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+             float scale, int is_causal, int dtype, void *stream);
+
+/*
+ * attn_fwd_validate -- the status attn_fwd would return for these arguments
+ * before launching (never HIP_ERROR). Makes no HIP call and dereferences no
+ * pointer, so it is usable without a GPU.
+ */
+int attn_fwd_validate(const void *q, const void *k, const void *v, void *o,
+                      const float *lse, int64_t B, int64_t H, int64_t M,
+                      int64_t N, int64_t D, float scale, int is_causal,
+                      int dtype);
+
+/*
+ * attn_fwd_path -- attn_fwd with an explicit kernel choice (one of the
+ * MI355_ATTN_PATH_* values). PATH_AUTO is attn_fwd. PATH_SMALL on a shape the
+ * small kernel cannot hold (see attn_fwd_select_path) returns UNSUPPORTED;
+ * an unknown path value returns INVALID_ARG. Results of the two paths agree
+ * to rounding; this exists so that each kernel can be checked on the same
+ * inputs.
+ */
+int attn_fwd_path(const void *q, const void *k, const void *v, void *o,
+                  float *lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                  int64_t D, float scale, int is_causal, int dtype, int path,
+                  void *stream);
+
+/*
+ * attn_fwd_select_path -- which kernel PATH_AUTO runs for this problem
+ * (MI355_ATTN_PATH_MAIN or MI355_ATTN_PATH_SMALL), or -1 if the sizes are
+ * invalid or unsupported. The small kernel holds one whole sequence per
+ * workgroup: it is chosen for M <= 64, N <= 64 and D <= 32. Pure host logic.
+ */
+int attn_fwd_select_path(int64_t B, int64_t H, int64_t M, int64_t N,
+                         int64_t D, int is_causal, int dtype);
+
+/* attn_status_string -- a static, NUL-terminated name for a status code
+ * ("unknown status" for values outside the list above). */
+const char *attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_ATTN_H */

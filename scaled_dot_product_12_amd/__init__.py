@@ -1,0 +1,149 @@
+"""Python binding of libmi355_attn (the C ABI in include/mi355_attn.h).
+
+Argument marshalling only: every step of the attention forward runs in the
+library's HIP kernels. torch provides device memory and the current stream.
+The C entry points are exposed under their own names; ``attn_fwd`` here takes
+torch tensors, allocates O and L, and calls the C ``attn_fwd`` on torch's
+current stream -- the interface of the pages' wrappers
+(``flash_attention_reference(Q, K, V, is_causal=False, scale=None) -> (O, L)``
+in "Extend Thunder with CUDA-Python"; ``(q, k, v) -> (o, lse)`` in
+"Blackwell Attention Example").
+
+There is no fallback: if the HIP library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmi355_attn.so")
+
+# Mirrors of the header's constants.
+MI355_ATTN_FP32 = 0
+MI355_ATTN_BF16 = 1
+MI355_ATTN_OK = 0
+MI355_ATTN_ERR_INVALID_ARG = 1
+MI355_ATTN_ERR_UNSUPPORTED = 2
+MI355_ATTN_ERR_MISALIGNED = 3
+MI355_ATTN_ERR_HIP = 4
+MI355_ATTN_PATH_AUTO = 0
+MI355_ATTN_PATH_MAIN = 1
+MI355_ATTN_PATH_SMALL = 2
+
+EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
+           "attn_fwd_select_path", "attn_status_string")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, cint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                               ctypes.c_float, cint, cint, vp]
+        L.attn_fwd.restype = cint
+        L.attn_fwd_path.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                    ctypes.c_float, cint, cint, cint, vp]
+        L.attn_fwd_path.restype = cint
+        L.attn_fwd_validate.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                        i64, ctypes.c_float, cint, cint]
+        L.attn_fwd_validate.restype = cint
+        L.attn_fwd_select_path.argtypes = [i64, i64, i64, i64, i64, cint, cint]
+        L.attn_fwd_select_path.restype = cint
+        L.attn_status_string.argtypes = [cint]
+        L.attn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def attn_fwd_validate(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype) -> int:
+    """Status attn_fwd would return; pointers are ints (addresses) or None."""
+    return lib().attn_fwd_validate(q, k, v, o, lse, B, H, M, N, D, float(scale),
+                                   int(is_causal), int(dtype))
+
+
+def attn_fwd_select_path(B, H, M, N, D, is_causal, dtype) -> int:
+    return lib().attn_fwd_select_path(B, H, M, N, D, int(is_causal), int(dtype))
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D) rounded to fp32, the value the C ABI receives by default."""
+    return ctypes.c_float(1.0 / math.sqrt(D)).value
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MI355_ATTN_FP32
+    if t.dtype == torch.bfloat16:
+        return MI355_ATTN_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _check(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, seq, D]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, M, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
+                         f"v {tuple(v.shape)}")
+    return B, H, M, k.shape[2], D
+
+
+def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
+             out: Optional[Tuple] = None,
+             path: int = MI355_ATTN_PATH_AUTO):
+    """(O, L) = attention forward of GPU tensors q [B,H,M,D], k, v [B,H,N,D].
+
+    O has q's dtype; L is fp32 [B,H,M], natural log. ``scale`` defaults to
+    1/sqrt(D). ``out=(o, lse)`` writes into preallocated tensors. ``path``
+    forces a kernel (MI355_ATTN_PATH_MAIN / _SMALL); the default lets the
+    library choose. The call is asynchronous on torch's current stream.
+    """
+    import torch
+    B, H, M, N, D = _check(q, k, v)
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+            raise ValueError("out[0] must be a contiguous tensor like q")
+        if (tuple(lse.shape) != (B, H, M) or lse.dtype != torch.float32
+                or not lse.is_contiguous()):
+            raise ValueError("out[1] must be a contiguous fp32 [B, H, M] tensor")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = lib().attn_fwd_path(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 o.data_ptr(), lse.data_ptr(), B, H, M, N, D,
+                                 float(scale), int(bool(is_causal)), dt,
+                                 int(path), stream)
+    if st != MI355_ATTN_OK:
+        raise RuntimeError(f"attn_fwd failed: {attn_status_string(st)} ({st})")
+    return o, lse

@@ -1,0 +1,152 @@
+// attn_api.cpp -- the C ABI declared in include/mi355_attn.h: argument
+// validation (pure host logic, no HIP call), kernel-path choice, and the
+// launch on the caller's stream.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/mi355_attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int64_t kIntMax = 2147483647;
+
+bool supported_d(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+// Byte ranges [p, p+n) and [r, r+m) intersect (empty ranges never do).
+bool overlap(const void* p, int64_t n, const void* r, int64_t m) {
+  if (n <= 0 || m <= 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)r;
+  return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+bool small_fits(int64_t M, int64_t N, int64_t D) { return M <= 64 && N <= 64 && D <= 32; }
+
+int validate(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+             int64_t D, float scale, int is_causal, int dtype) {
+  if (B < 0 || H < 0 || M < 0 || D < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (dtype != MI355_ATTN_FP32 && dtype != MI355_ATTN_BF16) return MI355_ATTN_ERR_INVALID_ARG;
+  if (is_causal != 0 && is_causal != 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MI355_ATTN_ERR_INVALID_ARG;
+  int64_t BH, rows;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, M, &rows)) return MI355_ATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return MI355_ATTN_OK;  // nothing to compute
+  if (N < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!supported_d(D)) return MI355_ATTN_ERR_UNSUPPORTED;
+
+  // Index types: per-head element offsets are 32-bit inside the kernels,
+  // head bases and the grid size are checked here.
+  const int64_t es = dtype == MI355_ATTN_FP32 ? 4 : 2;
+  int64_t md, nd, q_elems, kv_elems, q_bytes, kv_bytes, lse_bytes;
+  if (!mul_ok(M, D, &md) || !mul_ok(N, D, &nd) || md > kIntMax || nd > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (!mul_ok(rows, D, &q_elems) || !mul_ok(BH, nd, &kv_elems) ||
+      !mul_ok(q_elems, es, &q_bytes) || !mul_ok(kv_elems, es, &kv_bytes) ||
+      !mul_ok(rows, 4, &lse_bytes))
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  const int64_t tile = dtype == MI355_ATTN_FP32 ? mi355::main_f32_tile_rows()
+                                                : mi355::main_bf16_tile_rows();
+  int64_t grid;
+  if (!mul_ok((M + tile - 1) / tile, BH, &grid) || grid > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+    return MI355_ATTN_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3u) return MI355_ATTN_ERR_MISALIGNED;
+
+  // Outputs must not overlap the inputs or each other (inputs may alias).
+  if (overlap(o, q_bytes, q, q_bytes) || overlap(o, q_bytes, k, kv_bytes) ||
+      overlap(o, q_bytes, v, kv_bytes) || overlap(lse, lse_bytes, q, q_bytes) ||
+      overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, v, kv_bytes) ||
+      overlap(lse, lse_bytes, o, q_bytes))
+    return MI355_ATTN_ERR_INVALID_ARG;
+  return MI355_ATTN_OK;
+}
+
+int select_path(int64_t M, int64_t N, int64_t D) {
+  return small_fits(M, N, D) ? MI355_ATTN_PATH_SMALL : MI355_ATTN_PATH_MAIN;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_validate(const void* q, const void* k, const void* v, void* o,
+                      const float* lse, int64_t B, int64_t H, int64_t M,
+                      int64_t N, int64_t D, float scale, int is_causal,
+                      int dtype) {
+  return validate(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype);
+}
+
+int attn_fwd_select_path(int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                         int is_causal, int dtype) {
+  if (B < 0 || H < 0 || M < 0 || N < 1 || !supported_d(D)) return -1;
+  if (dtype != MI355_ATTN_FP32 && dtype != MI355_ATTN_BF16) return -1;
+  if (is_causal != 0 && is_causal != 1) return -1;
+  int64_t BH, rows;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, M, &rows)) return -1;
+  return select_path(M, N, D);
+}
+
+int attn_fwd_path(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                  int64_t D, float scale, int is_causal, int dtype, int path,
+                  void* stream) {
+  if (path != MI355_ATTN_PATH_AUTO && path != MI355_ATTN_PATH_MAIN &&
+      path != MI355_ATTN_PATH_SMALL)
+    return MI355_ATTN_ERR_INVALID_ARG;
+  const int st = validate(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype);
+  if (st != MI355_ATTN_OK) return st;
+  if (B * H * M == 0) return MI355_ATTN_OK;
+  if (path == MI355_ATTN_PATH_AUTO) path = select_path(M, N, D);
+  if (path == MI355_ATTN_PATH_SMALL && !small_fits(M, N, D)) return MI355_ATTN_ERR_UNSUPPORTED;
+
+  mi355::LaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = B * H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.causal = is_causal != 0;
+  a.stream = (hipStream_t)stream;
+  const bool bf16 = dtype == MI355_ATTN_BF16;
+  hipError_t err;
+  if (path == MI355_ATTN_PATH_SMALL)
+    err = mi355::launch_small(a, bf16);
+  else
+    err = bf16 ? mi355::launch_main_bf16(a) : mi355::launch_main_f32(a);
+  return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+             int is_causal, int dtype, void* stream) {
+  return attn_fwd_path(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype,
+                       MI355_ATTN_PATH_AUTO, stream);
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case MI355_ATTN_OK: return "ok";
+    case MI355_ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case MI355_ATTN_ERR_UNSUPPORTED: return "unsupported problem";
+    case MI355_ATTN_ERR_MISALIGNED: return "misaligned pointer";
+    case MI355_ATTN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// attn_device.h -- device-side building blocks shared by the gfx950
+// attention kernels: vector types, MFMA wrappers, wave64 half exchanges,
+// bf16 packing and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// log2(e) and ln(2) in fp32. The kernels run the softmax in base 2
+// (exp2 of log2(e)-scaled scores), the form used by the Blackwell attention
+// example, and convert the row logsumexp back to the natural log at the end.
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Lazy-rescale threshold in the log2 domain: the running reference max is
+// only moved (and O, l rescaled) once a row max exceeds it by more than this,
+// so the unnormalised probabilities stay below 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16_bf16(bf16x8_t a, bf16x8_t b,
+                                                        f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x2_f32(float a, float b,
+                                                      f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Lanes l and l^32 of a wave64 hold the two halves of one query row in the
+// kernels' layouts. permlane32_swap exchanges the halves; after a swap of x
+// with itself the two results at every lane are {x[l], x[l^32]} in some
+// order, so a symmetric combine of the pair is the half-pair combine.
+__device__ __forceinline__ float half_pair_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_pair_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round two fp32 values to bf16 (nearest-even) and pack them, lo first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// Wave-uniform "does any lane want this".
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin by workgroup id, and each
+// XCD has its own L2. Renumber them so that the ids one XCD receives form one
+// contiguous logical range: neighbouring logical tiles (the query tiles of one
+// head, which read the same K/V) then share an L2. Bijective for any count.
+__device__ __forceinline__ int xcd_contiguous_id(int wg, int count) {
+  const int xcd = wg & 7;
+  const int idx = wg >> 3;
+  const int per = count >> 3;
+  const int rem = count & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+}  // namespace mi355

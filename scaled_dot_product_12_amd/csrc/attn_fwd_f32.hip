@@ -1,0 +1,245 @@
+// attn_fwd_f32.hip -- FlashAttention-2 forward for fp32 inputs on gfx950.
+//
+// Same algorithm as the bf16 kernel (the tiled online softmax of "Extend
+// Thunder with CUDA-Python", Python reference section, run in base 2 as in
+// the "Blackwell Attention Example"), with every operand in fp32: both
+// products run on v_mfma_f32_32x32x2f32 (the fp32 matrix rate equals the fp32
+// vector rate on MI355X, and the MFMA needs no per-lane FMA chains), and P
+// stays fp32 for the second product.
+//
+// Differences from the bf16 kernel:
+//  * Q is multiplied by scale*log2(e) once, in fp32, when it is loaded into
+//    registers; scores come out of the MFMA already in the log2 domain, for
+//    any sign of the scale.
+//  * Key tiles are 32 wide. The second product contracts over two keys per
+//    MFMA (one per lane half), so its A operand (V^T) is one fp32 from a
+//    row-major V tile and V needs no transpose.
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace mi355 {
+
+template <int D, int WAVES, bool CAUSAL>
+__global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k,
+    const float* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
+    int M, int N, int tiles_m, float c) {
+  constexpr int NT = WAVES * 64;
+  constexpr int BM = WAVES * 32;
+  constexpr int BN = 32;
+  constexpr int HALF = D / 2;          // d values per lane half
+  constexpr int KSTR = D + 4;          // floats per K row in LDS
+  constexpr int DP = D < 32 ? 32 : D;  // V columns the O^T blocks read
+  constexpr int VSTR = DP + 2;         // floats per V row (rows 8-byte aligned)
+  constexpr int DBLK = DP / 32;
+  constexpr int DCH = D / 4;           // 16-byte chunks per row
+  constexpr int CH = BN * DCH;         // chunks per K (or V) tile
+  constexpr int CPT = (CH + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) float Ks[BN * KSTR];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int wl = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int bh = wl / tiles_m;
+  int tm = wl - bh * tiles_m;
+  if (CAUSAL) tm = tiles_m - 1 - tm;
+
+  const size_t q_off = (size_t)bh * M * D;
+  const size_t kv_off = (size_t)bh * N * D;
+  const float* qh = q + q_off;
+  const float* kh = k + kv_off;
+  const float* vh = v + kv_off;
+
+  const int q_wg0 = tm * BM;
+  const int qw0 = q_wg0 + wave * 32;
+  const int qi = qw0 + r32;
+  const bool wave_live = qw0 < M;
+  const int wave_last = min(qw0 + 31, M - 1);
+
+  // Q^T as the B operand, pre-scaled: lane holds c*Q[qi][g*HALF + t].
+  float qf[HALF];
+#pragma unroll
+  for (int t4 = 0; t4 < HALF / 4; ++t4) {
+    f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (qi < M) x = *(const f32x4_t*)(qh + (size_t)qi * D + g * HALF + t4 * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qf[t4 * 4 + e] = x[e] * c;
+  }
+
+  int nt = (N + BN - 1) / BN;
+  if (CAUSAL) {
+    const int q_last = min(q_wg0 + BM, M) - 1;
+    nt = min(nt, q_last / BN + 1);
+  }
+
+  if (D < 32) {  // V columns D..31 stay zero
+    for (int idx = tid; idx < BN * (DP - D); idx += NT) {
+      const int row = idx / (DP - D);
+      Vs[row * VSTR + D + (idx - row * (DP - D))] = 0.0f;
+    }
+  }
+
+  f32x4_t kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int j) {
+    const int key0 = j * BN;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ch = tid + u * NT;
+      if (ch < CH) {
+        const int row = ch / DCH;
+        const int col = (ch - row * DCH) * 4;
+        const int key = key0 + row;
+        f32x4_t xk = {0.0f, 0.0f, 0.0f, 0.0f}, xv = xk;
+        if (key < N) {
+          xk = *(const f32x4_t*)(kh + (size_t)key * D + col);
+          xv = *(const f32x4_t*)(vh + (size_t)key * D + col);
+        }
+        kreg[u] = xk;
+        vreg[u] = xv;
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ch = tid + u * NT;
+      if (ch < CH) {
+        const int row = ch / DCH;
+        const int col = (ch - row * DCH) * 4;
+        *(f32x4_t*)(Ks + row * KSTR + col) = kreg[u];
+        f32x2_t lo = {vreg[u][0], vreg[u][1]}, hi = {vreg[u][2], vreg[u][3]};
+        *(f32x2_t*)(Vs + row * VSTR + col) = lo;
+        *(f32x2_t*)(Vs + row * VSTR + col + 2) = hi;
+      }
+    }
+  };
+
+  const int krow = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
+
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  f32x16_t acc[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+
+  if (nt > 0) load_tile(0);
+  for (int j = 0; j < nt; ++j) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (j + 1 < nt) load_tile(j + 1);
+    const int key0 = j * BN;
+    if (!wave_live) continue;
+    if (CAUSAL && key0 > wave_last) continue;
+
+    // S^T = K (cQ)^T, one 32-key block: lane owns keys g*16 + i.
+    f32x16_t s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+    const float* kp = Ks + krow * KSTR + g * HALF;
+#pragma unroll
+    for (int t4 = 0; t4 < HALF / 4; ++t4) {
+      const f32x4_t a = *(const f32x4_t*)(kp + t4 * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mfma_32x32x2_f32(a[e], qf[t4 * 4 + e], s);
+    }
+    const bool need_mask = (key0 + BN > N) || (CAUSAL && key0 + BN - 1 > qw0);
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + g * 16 + i;
+        if (key >= N || (CAUSAL && key > qi)) s[i] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = half_pair_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (wave_any(m_new > m_run + kRescaleThreshold)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
+    float p[16];
+    float rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(s[i] - m_sub);
+      rs += p[i];
+    }
+    l_run += rs;
+
+    // O^T += V^T P^T: MFMA t contracts keys t (lanes 0-31) and 16+t (32-63).
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+      const float* vp = Vs + (g * 16) * VSTR + b * 32 + r32;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc[b] = mfma_32x32x2_f32(vp[t * VSTR], p[t], acc[b]);
+    }
+  }
+
+  if (!wave_live) return;
+  const float l_tot = half_pair_sum(l_run);
+  if (qi >= M) return;
+  const float inv = 1.0f / l_tot;
+  float* orow = o + q_off + (size_t)qi * D;
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = b * 32 + i4 * 8 + g * 4;
+      if (d0 < D) {
+        f32x4_t st = {acc[b][i4 * 4 + 0] * inv, acc[b][i4 * 4 + 1] * inv,
+                      acc[b][i4 * 4 + 2] * inv, acc[b][i4 * 4 + 3] * inv};
+        *(f32x4_t*)(orow + d0) = st;
+      }
+    }
+  if (g == 0) lse[(size_t)bh * M + qi] = (m_run + log2f(l_tot)) * kLn2;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_f32_d(const LaunchArgs& a) {
+  constexpr int WAVES = 4;
+  constexpr int BM = WAVES * 32;
+  const int tiles_m = (int)((a.M + BM - 1) / BM);
+  const dim3 grid((unsigned)(tiles_m * a.BH));
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, WAVES, CAUSAL>), grid,
+                     dim3(WAVES * 64), 0, a.stream, (const float*)a.q,
+                     (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                     (int)a.M, (int)a.N, tiles_m, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_f32_dispatch(const LaunchArgs& a) {
+  return a.causal ? launch_f32_d<D, true>(a) : launch_f32_d<D, false>(a);
+}
+
+hipError_t launch_main_f32(const LaunchArgs& a) {
+  switch (a.D) {
+    case 16: return launch_f32_dispatch<16>(a);
+    case 32: return launch_f32_dispatch<32>(a);
+    case 64: return launch_f32_dispatch<64>(a);
+    case 128: return launch_f32_dispatch<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int main_f32_tile_rows() { return 4 * 32; }
+
+}  // namespace mi355

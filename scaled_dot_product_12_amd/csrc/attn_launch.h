@@ -1,0 +1,33 @@
+// attn_launch.h -- internal interface between the C ABI (attn_api.cpp) and
+// the kernel launchers. Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+struct LaunchArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t BH;  // B * H
+  int64_t M, N, D;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+// Tiled MFMA kernels with the online softmax (any M, N >= 1).
+hipError_t launch_main_bf16(const LaunchArgs& a);
+hipError_t launch_main_f32(const LaunchArgs& a);
+// One-tile LDS-resident kernel (M <= 64, N <= 64, D <= 32).
+hipError_t launch_small(const LaunchArgs& a, bool bf16);
+
+// Query rows per workgroup of the main kernels (grid sizing checks).
+int main_bf16_tile_rows();
+int main_f32_tile_rows();
+
+}  // namespace mi355

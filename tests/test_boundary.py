@@ -1,0 +1,162 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and every argument check returns its status before any HIP call
+(attn_fwd_validate / attn_fwd_select_path are pure host logic)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355_attn.h")
+
+FP32, BF16 = 0, 1
+OK, INVALID, UNSUPPORTED, MISALIGNED, HIPERR = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
+         "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol(hip_lib):
+    lib = hip_lib.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", hip_lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(hip_lib.EXPORTS) == set(declared_functions())
+
+
+def test_header_constants_match_binding(hip_lib):
+    text = open(HEADER).read()
+    for name, val in re.findall(r"#define\s+(MI355_ATTN_\w+)\s+(\d+)", text):
+        assert getattr(hip_lib, name) == int(val), name
+
+
+# Stand-in addresses: never dereferenced (validation makes no HIP call).
+A = 1 << 20
+SZ = 1 << 34  # far apart, so none of the buffers below overlap
+
+
+def ptrs():
+    return A, A + SZ, A + 2 * SZ, A + 3 * SZ, A + 4 * SZ
+
+
+def val(hip_lib, *, q=None, k=None, v=None, o=None, lse=None, B=2, H=3, M=100,
+        N=70, D=64, scale=0.125, causal=0, dtype=BF16):
+    p = ptrs()
+    q = p[0] if q is None else q
+    k = p[1] if k is None else k
+    v = p[2] if v is None else v
+    o = p[3] if o is None else o
+    lse = p[4] if lse is None else lse
+    return hip_lib.attn_fwd_validate(q, k, v, o, lse, B, H, M, N, D, scale, causal, dtype)
+
+
+def test_valid_arguments(hip_lib):
+    for dtype in (FP32, BF16):
+        for D in (16, 32, 64, 128):
+            for causal in (0, 1):
+                assert val(hip_lib, D=D, dtype=dtype, causal=causal) == OK
+
+
+def test_invalid_arguments(hip_lib):
+    assert val(hip_lib, q=0) == INVALID
+    assert val(hip_lib, k=0) == INVALID
+    assert val(hip_lib, v=0) == INVALID
+    assert val(hip_lib, o=0) == INVALID
+    assert val(hip_lib, lse=0) == INVALID
+    assert val(hip_lib, B=-1) == INVALID
+    assert val(hip_lib, H=-1) == INVALID
+    assert val(hip_lib, M=-1) == INVALID
+    assert val(hip_lib, N=0) == INVALID
+    assert val(hip_lib, N=-5) == INVALID
+    assert val(hip_lib, D=0) == INVALID
+    assert val(hip_lib, causal=2) == INVALID
+    assert val(hip_lib, causal=-1) == INVALID
+    assert val(hip_lib, dtype=2) == INVALID
+    assert val(hip_lib, scale=float("inf")) == INVALID
+    assert val(hip_lib, scale=float("nan")) == INVALID
+
+
+def test_unsupported(hip_lib):
+    for D in (1, 8, 48, 96, 256):
+        assert val(hip_lib, D=D) == UNSUPPORTED
+    assert val(hip_lib, M=1 << 40) == UNSUPPORTED           # M*D beyond 32-bit
+    assert val(hip_lib, B=1 << 40, H=1 << 40) == UNSUPPORTED  # B*H overflows
+
+
+def test_misaligned(hip_lib):
+    p = ptrs()
+    assert val(hip_lib, q=p[0] + 8) == MISALIGNED
+    assert val(hip_lib, k=p[1] + 2) == MISALIGNED
+    assert val(hip_lib, v=p[2] + 4) == MISALIGNED
+    assert val(hip_lib, o=p[3] + 8) == MISALIGNED
+    assert val(hip_lib, lse=p[4] + 2) == MISALIGNED
+    assert val(hip_lib, lse=p[4] + 4) == OK  # fp32 alignment is enough for L
+
+
+def test_overlaps(hip_lib):
+    p = ptrs()
+    assert val(hip_lib, o=p[0]) == INVALID            # o on q
+    assert val(hip_lib, o=p[1] + 256) == INVALID      # o inside k
+    assert val(hip_lib, lse=p[2] + 64) == INVALID     # lse inside v
+    assert val(hip_lib, lse=p[3] + 1024) == INVALID   # lse inside o
+    assert val(hip_lib, k=p[0], v=p[0]) == OK         # inputs may alias
+    # o ends exactly where lse starts: adjacent, not overlapping
+    o_bytes = 2 * 3 * 100 * 64 * 2
+    assert val(hip_lib, lse=p[3] + o_bytes) == OK
+    assert val(hip_lib, lse=p[3] + o_bytes - 4) == INVALID
+
+
+def test_empty_problems_are_ok(hip_lib):
+    assert val(hip_lib, B=0, q=0, k=0, v=0, o=0, lse=0) == OK
+    assert val(hip_lib, H=0, q=0, k=0, v=0, o=0, lse=0) == OK
+    assert val(hip_lib, M=0, N=0, q=0, k=0, v=0, o=0, lse=0) == OK
+    # empty but with a bad flag is still rejected
+    assert val(hip_lib, M=0, causal=3) == INVALID
+
+
+def test_select_path(hip_lib):
+    f = hip_lib.attn_fwd_select_path
+    SMALL, MAIN = hip_lib.MI355_ATTN_PATH_SMALL, hip_lib.MI355_ATTN_PATH_MAIN
+    assert f(128, 4, 32, 32, 16, 0, FP32) == SMALL   # axial pass
+    assert f(1, 1, 64, 64, 32, 1, BF16) == SMALL
+    assert f(1, 1, 128, 128, 64, 0, FP32) == MAIN    # single head fp32
+    assert f(96, 1, 512, 512, 128, 0, FP32) == MAIN
+    assert f(4, 16, 4096, 4096, 128, 0, BF16) == MAIN
+    assert f(1, 1, 65, 32, 16, 0, FP32) == MAIN
+    assert f(1, 1, 32, 32, 64, 0, FP32) == MAIN
+    assert f(1, 1, 32, 0, 16, 0, FP32) == -1
+    assert f(1, 1, 32, 32, 24, 0, FP32) == -1
+    assert f(1, 1, 32, 32, 16, 0, 7) == -1
+
+
+def test_status_strings(hip_lib):
+    names = {OK: "ok", INVALID: "invalid argument", UNSUPPORTED: "unsupported problem",
+             MISALIGNED: "misaligned pointer", HIPERR: "HIP launch error"}
+    for code, s in names.items():
+        assert hip_lib.attn_status_string(code) == s
+    assert hip_lib.attn_status_string(99) == "unknown status"
+    assert hip_lib.attn_status_string(-1) == "unknown status"
+
+
+def test_python_wrapper_rejects_before_any_gpu_call(hip_lib):
+    q = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        hip_lib.attn_fwd(q, q, q)                     # CPU tensors
+    with pytest.raises(ValueError):
+        hip_lib.attn_fwd(q.half(), q.half(), q.half())  # not a GPU tensor either
+    assert hip_lib.default_scale(128) == ctypes.c_float(128 ** -0.5).value

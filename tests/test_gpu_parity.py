@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Tolerances (max abs over every compared element): fp32 inputs O <= 2e-5,
+L <= 1e-5; bf16 inputs (oracle on the same bf16 values) O <= 2e-2,
+L <= 1e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_12_amd as attn
+from scaled_dot_product_12_amd.inputs import WORKLOADS, make_qkv, workload_inputs
+from parity_util import TOL, check_full, check_sampled, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+MAIN, SMALL = attn.MI355_ATTN_PATH_MAIN, attn.MI355_ATTN_PATH_SMALL
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+# --------------------------------------------- shapes spanning tiles + tails
+SHAPES = [  # (B, H, M, N): several query / key tiles and ragged tails
+    (1, 2, 300, 300),
+    (2, 1, 17, 1000),
+    (1, 1, 600, 33),
+    (1, 1, 1, 1),
+    (1, 3, 1, 130),
+    (1, 1, 257, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_main_kernel_shapes(dtype, D, causal):
+    for i, (B, H, M, N) in enumerate(SHAPES):
+        q, k, v = make_qkv(B, H, M, N, D, dtype, seed=1000 + i + D)
+        check_full(q, k, v, causal, f32(1 / math.sqrt(D)), path=MAIN,
+                   label=f"shape{i}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [16, 32])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_kernel_shapes(dtype, D, causal):
+    for i, (B, H, M, N) in enumerate([(3, 2, 32, 32), (1, 1, 64, 64), (2, 1, 1, 1),
+                                      (1, 2, 5, 64), (1, 1, 64, 3), (2, 2, 17, 45)]):
+        q, k, v = make_qkv(B, H, M, N, D, dtype, seed=2000 + i + D)
+        check_full(q, k, v, causal, f32(1 / math.sqrt(D)), path=SMALL,
+                   label=f"small{i}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("scale", [0.0, -0.3, 1.7])
+def test_scale_values(dtype, scale):
+    """Scales other than 1/sqrt(D): zero, negative, and large (|L| ~ 40, where
+    the fp32 bounds widen with the magnitude of the scores)."""
+    q, k, v = make_qkv(1, 2, 200, 150, 64, dtype, seed=31)
+    for causal in (False, True):
+        check_full(q, k, v, causal, f32(scale), path=MAIN, label=f"scale{scale}",
+                   magnitude_tol=True)
+    q, k, v = make_qkv(2, 2, 32, 32, 16, dtype, seed=32)
+    check_full(q, k, v, False, f32(scale), path=SMALL, label=f"small-scale{scale}",
+               magnitude_tol=True)
+
+
+# ---------------------------------------------------------- the workloads
+@pytest.mark.parametrize("name", ["c1", "c2", "c2c", "c3r", "c3c"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    check_full(q, k, v, w.causal, w.scale, label=name)
+    if w.axial:  # the axial passes also through the main kernel
+        check_full(q, k, v, w.causal, w.scale, path=MAIN, label=name + "-main")
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_workload_sampled(name):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    o, lse = check_sampled(q, k, v, w.causal, w.scale, n_random=400, seed=w.seed,
+                           label=name)
+    # Properties that hold for every row at full size: finite, and the
+    # oracle's bound max_j s_ij <= L_i <= max_j s_ij + ln|J_i| for row 0 of
+    # each head where the causal row 0 has a single key.
+    if w.causal:
+        v0 = v[:, :, 0].float().numpy()
+        assert np.abs(o[:, :, 0] - v0).max() <= TOL["bf16"][0]
+        l0 = w.scale * (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1).numpy()
+        assert np.abs(lse[:, :, 0] - l0).max() <= TOL["bf16"][1]
+
+
+# ------------------------------------------------------------- invariants
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_constant_v_and_causal_row0(dtype):
+    q, k, _ = make_qkv(1, 2, 300, 300, 128, dtype, seed=41)
+    v = torch.full(k.shape, 0.75, dtype=k.dtype)
+    o, _ = run_gpu(q, k, v, True, f32(0.1))
+    assert np.abs(o - 0.75).max() <= (1e-6 if dtype == "fp32" else 4e-3)
+    q, k, v = make_qkv(1, 2, 300, 300, 128, dtype, seed=42)
+    scale = f32(0.1)
+    o, lse = run_gpu(q, k, v, True, scale)
+    assert np.abs(o[:, :, 0] - v[:, :, 0].double().numpy()).max() <= 2e-6
+    ref_l0 = scale * (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1).numpy()
+    assert np.abs(lse[:, :, 0] - ref_l0).max() <= TOL[dtype][1]
+
+
+def test_key_shift_invariance_fp32():
+    """Adding u to every key adds scale*q.u to each row's scores: O unchanged,
+    L shifted by scale*q.u (checked on the GPU outputs themselves)."""
+    q, k, v = make_qkv(1, 2, 200, 300, 64, "fp32", seed=43)
+    u = torch.linspace(-0.5, 0.5, 64)
+    scale = f32(0.125)
+    o1, l1 = run_gpu(q, k, v, False, scale)
+    o2, l2 = run_gpu(q, k + u, v, False, scale)
+    shift = scale * (q.double() @ u.double()).numpy()
+    assert np.abs(o1 - o2).max() <= 4e-5
+    assert np.abs((l2 - l1) - shift).max() <= 2e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_deterministic_and_no_stray_writes(dtype):
+    """Two runs are bitwise identical; guard bands around O and L stay
+    untouched; poisoned outputs are fully overwritten."""
+    B, H, M, N, D = 2, 3, 333, 200, 128
+    q, k, v = make_qkv(B, H, M, N, D, dtype, seed=44)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    tdt = qd.dtype
+    res = []
+    for causal in (False, True):
+        for rep in range(2):
+            n_o, n_l = B * H * M * D, B * H * M
+            pad = 4096
+            obuf = torch.full((n_o + 2 * pad,), float("nan"), dtype=tdt, device=dev)
+            lbuf = torch.full((n_l + 2 * pad,), float("nan"), dtype=torch.float32, device=dev)
+            obuf[:pad] = 7.0
+            obuf[-pad:] = 7.0
+            lbuf[:pad] = 7.0
+            lbuf[-pad:] = 7.0
+            o = obuf[pad:pad + n_o].view(B, H, M, D)
+            lse = lbuf[pad:pad + n_l].view(B, H, M)
+            attn.attn_fwd(qd, kd, vd, is_causal=causal, out=(o, lse))
+            torch.cuda.synchronize()
+            assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+            assert (obuf[:pad] == 7.0).all() and (obuf[-pad:] == 7.0).all()
+            assert (lbuf[:pad] == 7.0).all() and (lbuf[-pad:] == 7.0).all()
+            res.append((o.clone(), lse.clone()))
+        assert torch.equal(res[-1][0], res[-2][0]) and torch.equal(res[-1][1], res[-2][1])
+
+
+def test_paths_agree_on_small_shapes():
+    q, k, v = make_qkv(4, 4, 32, 32, 16, "fp32", seed=45)
+    a = run_gpu(q, k, v, False, f32(0.25), path=SMALL)
+    b = run_gpu(q, k, v, False, f32(0.25), path=MAIN)
+    assert np.abs(a[0] - b[0]).max() <= 2e-5 and np.abs(a[1] - b[1]).max() <= 1e-5
+
+
+def test_empty_problem_launches_nothing():
+    dev = torch.device("cuda:0")
+    q = torch.zeros(0, 2, 16, 64, device=dev)
+    o, lse = attn.attn_fwd(q, q, q)
+    assert o.shape == (0, 2, 16, 64) and lse.shape == (0, 2, 16)
+    q = torch.zeros(1, 2, 0, 64, device=dev)
+    k = torch.zeros(1, 2, 5, 64, device=dev)
+    o, lse = attn.attn_fwd(q, k, k)
+    assert o.shape == (1, 2, 0, 64)
+
+
+def test_small_path_rejects_large_shapes():
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 1, 65, 16, device=dev)
+    with pytest.raises(RuntimeError, match="unsupported"):
+        attn.attn_fwd(q, q, q, path=SMALL)
