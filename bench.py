@@ -46,7 +46,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times "
+                         "(reference reading for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 5}))
 
 
 def kernel_source_hash() -> str:
@@ -204,6 +219,9 @@ def main():
     import torch
     import __graft_entry__ as ge
     from scaled_dot_product_12_amd.inputs import WORKLOADS
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
     ge.ensure_built()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -31,9 +31,16 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950",
           "-Wall", "-I", os.path.join(ROOT, "include")]
 
 
+# Kernel sources: no IEEE NaN-quieting of min/max operands (the kernels take
+# no NaN-specific decisions; this keeps the row-max trees free of extra
+# canonicalising moves).
+KERNEL_FLAGS = ["-mno-amdgpu-ieee", "-fno-honor-nans"]
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    cmd = [hipcc()] + COMMON + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
