@@ -91,12 +91,19 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, graph=False):
+def time_launches(fn, steps, warmup, graph=False, spin_s=1.0):
     """Average GPU time per call (ms) with HIP events on the launch stream.
     graph=True captures the calls in one HIP graph first (for microsecond
     kernels whose Python launch cost would otherwise leave the GPU idle)."""
     import torch
     stream = torch.cuda.current_stream()
+    # Spin the GPU up to its sustained clock before the warmup proper, so the
+    # timed steps do not include the power-state ramp.
+    t_end = time.perf_counter() + spin_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()

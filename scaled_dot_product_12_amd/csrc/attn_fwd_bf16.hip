@@ -54,6 +54,11 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t __attribute__((address_space(3)))*)(lds_u8*)p);
 }
 
+// An empty volatile asm statement: a branch body containing it cannot be
+// if-converted into unconditional selects, so the rarely taken wave-uniform
+// paths (masking, O rescale) stay off the per-tile instruction stream.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
 }  // namespace
 
 // Waves per workgroup: two per SIMD, one of each ping-pong group.
@@ -210,39 +215,60 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
   f32x16_t s_cur[2];  // scores of the tile in flight
 
+  // Operand fragments are read from LDS PF MFMAs ahead of their use (a ring
+  // of PF+1 register fragments), and consecutive MFMAs go to independent
+  // accumulators, so LDS latency overlaps matrix work.
+  constexpr int PF = 3;
+
+  // S^T = K Q^T for the 64-key tile in buffer buf: fragment i is key block
+  // kb = i & 1 at d-step t = i >> 1.
   auto qk = [&](int buf, f32x16_t* s) {
     const unsigned char* kb_base = smem + buf * TILEB + k_rd;
+    constexpr int NF = 2 * QSTEPS;
+    auto frag = [&](int i) -> u32x4_t {
+      const int t = i >> 1, kb = i & 1;
+      return *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+    u32x4_t fr[PF + 1];
 #pragma unroll
-      for (int t = 0; t < QSTEPS; ++t) {
-        const u32x4_t a = *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
-        s[kb] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[t], s[kb]);
-      }
+    for (int i = 0; i < PF && i < NF; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      if (i + PF < NF) fr[(i + PF) % (PF + 1)] = frag(i + PF);
+      s[i & 1] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (PF + 1)]), qf[i >> 1],
+                                    s[i & 1]);
     }
   };
 
+  // O^T += V^T P^T for the tile in V buffer buf: fragment i is O block
+  // b = i % DBLK of key step (kb, t) = ((i / DBLK) >> 1, (i / DBLK) & 1).
   auto pv = [&](int buf, const u32x4_t (*p)[2]) {
     const unsigned char* vb_base = smem + C::V_OFF + buf * TILEB;
     const unsigned char* zero = smem + C::ZERO_OFF;
+    constexpr int NF = 4 * DBLK;
+    typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+    auto frag = [&](int i) -> s16x8_t {
+      const int b = i % DBLK, kt = i / DBLK, kb = kt >> 1, t = kt & 1;
+      const int row_off = (kb * 32 + t * 8) * ROWB;
+      const unsigned char* a0 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off;
+      const unsigned char* a1 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off + 4 * ROWB;
+      const s16x4_t lo = lds_read_tr16(a0);
+      const s16x4_t hi = lds_read_tr16(a1);
+      return (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    s16x8_t fr[PF + 1];
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
+    for (int i = 0; i < PF && i < NF; ++i) fr[i] = frag(i);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int row_off = (kb * 32 + t * 8) * ROWB;
-          const unsigned char* a0 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off;
-          const unsigned char* a1 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off + 4 * ROWB;
-          const s16x4_t lo = lds_read_tr16(a0);
-          const s16x4_t hi = lds_read_tr16(a1);
-          typedef __attribute__((ext_vector_type(8))) short s16x8_t;
-          const s16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[b] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                      __builtin_bit_cast(bf16x8_t, p[kb][t]), acc[b]);
-        }
+    for (int i = 0; i < NF; ++i) {
+      if (i + PF < NF) fr[(i + PF) % (PF + 1)] = frag(i + PF);
+      const int b = i % DBLK, kt = i / DBLK;
+      acc[b] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (PF + 1)]),
+                                  __builtin_bit_cast(bf16x8_t, p[kt >> 1][kt & 1]), acc[b]);
     }
   };
 
@@ -263,6 +289,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
         for (int i = 0; i < 16; ++i) s[kb][i] *= c;
     }
     if (mask) {
+      keep_branch();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -332,7 +359,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
     float rs = tile_exp(s[0], st.m_sub, p[0]);
     rs += tile_exp(s[1], st.m_sub, p[1]);
     l_run = (st.resc ? l_run * st.alpha : l_run) + rs;
-    if (st.resc) rescale(st.alpha);
+    if (st.resc) {
+      keep_branch();
+      rescale(st.alpha);
+    }
     pv(j % C::VBUF, p);
   };
 
