@@ -60,6 +60,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Work-item and workgroup index from the hardware registers. The kernels are
+// built with -mno-amdgpu-ieee, which the device library's threadIdx/blockIdx
+// accessors are not, so those accessors stay out-of-line calls; the builtins
+// below are single register reads.
+__device__ __forceinline__ int workitem_id() {
+  return (int)__builtin_amdgcn_workitem_id_x();
+}
+__device__ __forceinline__ int workgroup_id() {
+  return (int)__builtin_amdgcn_workgroup_id_x();
+}
+
 // Wave-uniform "does any lane want this".
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;

@@ -94,20 +94,20 @@ template <int D, int WAVES, bool CAUSAL, bool POS_SCALE>
 __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int M, int N, int tiles_m, float c) {
+    float* __restrict__ lse, int M, int N, int tiles_m, int n_wg, float c) {
   using C = Bf16Cfg<D, WAVES>;
   constexpr int NT = C::NT, BM = C::BM, BN = C::BN, ROWB = C::ROWB,
                 TILEB = C::TILEB, CPT = C::CPT, QSTEPS = C::QSTEPS, DBLK = C::DBLK;
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
 
-  const int tid = threadIdx.x;
+  const int tid = workitem_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  const int wl = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int wl = xcd_contiguous_id(workgroup_id(), n_wg);
   const int bh = wl / tiles_m;
   int tm = wl - bh * tiles_m;
   if (CAUSAL) tm = tiles_m - 1 - tm;  // longest rows first
@@ -433,7 +433,7 @@ static hipError_t launch_bf16_d(const LaunchArgs& a) {
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, WAVES, CAUSAL, POS>), grid,
                      dim3(WAVES * 64), 0, a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                     a.lse, (int)a.M, (int)a.N, tiles_m, a.scale * kLog2e);
+                     a.lse, (int)a.M, (int)a.N, tiles_m, tiles_m * (int)a.BH, a.scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -1,22 +1,30 @@
 // attn_fwd_small.hip -- attention forward for short sequences with small
-// heads (M <= 64, N <= 64, D <= 32), e.g. the axial-attention passes of the
-// PopcornBench trajectory (32 tokens per row or column, head dim 16).
+// heads (M <= 64, N <= 64, D in {16, 32}), e.g. the axial-attention passes of
+// the PopcornBench trajectory (32 tokens per row or column, head dim 16).
 //
-// Such a problem is one tile: the whole of Q, K and V for one (batch, head)
-// fits in LDS, so there is no online rescaling -- the softmax is taken once
-// over the full row, which is the Python reference's loop ("Extend Thunder
-// with CUDA-Python") with a single key tile. The work per head is tiny, so
-// the bound is HBM latency and bandwidth, not arithmetic: every thread issues
-// its global loads at once, the arithmetic runs in fp32 on the vector units
-// out of LDS, and the results leave with one store per thread.
+// Such a problem is one tile: all of K and V for one (batch, head) fit in the
+// registers of one wave, so there is no online rescaling -- the softmax is
+// taken once over the full row, which is the Python reference's loop
+// ("Extend Thunder with CUDA-Python") with a single key tile. The work per
+// head is tiny, so the bound is latency (launch, one round trip to HBM), not
+// arithmetic or bandwidth. The kernel therefore has a single phase with no
+// barrier and no LDS: every lane issues all its global loads at once, in the
+// exact operand layout of the fp32 MFMA, and both products run on the matrix
+// cores (fp32 in, fp32 accumulate -- no precision is given up on fp32 inputs).
 //
-// One workgroup of 256 threads per (batch, head). Phases, separated by
-// barriers:
-//   1. Q, K, V -> LDS as fp32 (bf16 inputs widened exactly).
-//   2. S = Q K^T * scale*log2(e) for all (row, key) pairs.
-//   3. per row: max, p = exp2(s - max), sum -- 4 threads per row with
-//      in-wave butterfly reductions; L = ln2 * (max + log2 sum).
-//   4. O = P V / sum for all (row, d) pairs, then stored.
+// One workgroup per (batch, head); one wave per block of 16 query rows.
+// With v_mfma_f32_16x16x4_f32, lane l = 16 g + n (n = l % 16, g = l / 16):
+//   S^T block kb (keys 16 kb .. 16 kb + 15 by queries q0 .. q0 + 15)
+//     A = K rows,   lane supplies K[16 kb + n][d],  d = g * D/4 + t
+//     B = Q^T,      lane supplies Q[q0 + n][d]      (same d: the contraction
+//                                                    order over d is free)
+//     result: lane holds S for query q0 + n and keys 16 kb + 4 g + r, r < 4.
+//   Row max / sum over the four lanes n, n+16, n+32, n+48 (permlane swaps).
+//   O^T block db (d = 16 db .. 16 db + 15 by the 16 queries)
+//     A = V^T,      lane supplies V[16 kb + 4 g + r][16 db + n]
+//     B = P^T,      lane supplies its own P for key 16 kb + 4 g + r
+//     result: lane holds O[q0 + n][16 db + 4 g + r], r < 4 -- one 16-byte
+//     (fp32) or 8-byte (bf16) store per block.
 
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -27,131 +35,187 @@ namespace {
 constexpr int kSmallMaxM = 64;
 constexpr int kSmallMaxN = 64;
 constexpr int kSmallMaxD = 32;
-constexpr int kSmallThreads = 256;
-}  // namespace
+constexpr int kSmallMaxKB = kSmallMaxN / 16;
+constexpr int kSmallQRows = 16;  // query rows per wave
 
-template <bool BF16>
-__global__ __launch_bounds__(kSmallThreads) void attn_fwd_small_kernel(
-    const void* __restrict__ qv, const void* __restrict__ kv,
-    const void* __restrict__ vv, void* __restrict__ ov, float* __restrict__ lse,
-    int M, int N, int D, int causal, float c) {
-  constexpr int SP = kSmallMaxN + 1;  // S row stride (odd: no bank repeats)
-  constexpr int XP = kSmallMaxD + 1;  // Q/K/V row stride
-  __shared__ float Qs[kSmallMaxM * XP];
-  __shared__ float Ks[kSmallMaxN * XP];
-  __shared__ float Vs[kSmallMaxN * XP];
-  __shared__ float Ss[kSmallMaxM * SP];
-  __shared__ float Rinv[kSmallMaxM];
+__device__ __forceinline__ f32x4_t mfma_16x16x4_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
-  const int tid = threadIdx.x;
-  const size_t bh = blockIdx.x;
-  const size_t q_off = bh * (size_t)M * D;
-  const size_t kv_off = bh * (size_t)N * D;
+// Symmetric combines over the lane pairs l, l ^ 16 (permlane16_swap) and
+// l, l ^ 32 (permlane32_swap): after a swap of x with itself each lane holds
+// {x[l], x[partner]} in some order.
+__device__ __forceinline__ float pair16_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-  // 1. Stage Q, K, V. Each element is a (row, d) pair; four per step.
-  const int qn = M * D, kn = N * D;
-  for (int e4 = tid * 4; e4 < qn + 2 * kn; e4 += kSmallThreads * 4) {
-    // D is a multiple of 16 and the three tensors are consecutive ranges of
-    // e4, so a group of four never straddles a row or a tensor boundary.
-    const int which = e4 < qn ? 0 : (e4 < qn + kn ? 1 : 2);
-    const int e = which == 0 ? e4 : (which == 1 ? e4 - qn : e4 - qn - kn);
-    const size_t base = (which == 0 ? q_off : kv_off) + e;
-    const void* src = which == 0 ? qv : (which == 1 ? kv : vv);
-    float x[4];
-    if (BF16) {
-      const u32x2_t w = *(const u32x2_t*)((const uint16_t*)src + base);
-      x[0] = __uint_as_float(w[0] << 16);
-      x[1] = __uint_as_float(w[0] & 0xffff0000u);
-      x[2] = __uint_as_float(w[1] << 16);
-      x[3] = __uint_as_float(w[1] & 0xffff0000u);
-    } else {
-      const f32x4_t w = *(const f32x4_t*)((const float*)src + base);
-      x[0] = w[0]; x[1] = w[1]; x[2] = w[2]; x[3] = w[3];
-    }
-    const int row = e / D, col = e - (e / D) * D;
-    float* dst = (which == 0 ? Qs : (which == 1 ? Ks : Vs)) + row * XP + col;
-    dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
-  }
-  __syncthreads();
-
-  // 2. Scores in the log2 domain; masked entries -inf.
-  for (int idx = tid; idx < M * N; idx += kSmallThreads) {
-    const int i = idx / N, j = idx - (idx / N) * N;
-    const float* qr = Qs + i * XP;
-    const float* kr = Ks + j * XP;
-    float dot = 0.0f;
-    for (int d = 0; d < D; ++d) dot = fmaf(qr[d], kr[d], dot);
-    Ss[i * SP + j] = (causal && j > i) ? -INFINITY : dot * c;
-  }
-  __syncthreads();
-
-  // 3. Row statistics: 4 consecutive lanes per row (M <= 64 rows).
-  {
-    const int i = tid >> 2, part = tid & 3;
-    float mx = -INFINITY;
-    if (i < M)
-      for (int j = part; j < N; j += 4) mx = fmaxf(mx, Ss[i * SP + j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    const float m_sub = (mx == -INFINITY) ? 0.0f : mx;
-    float sum = 0.0f;
-    if (i < M)
-      for (int j = part; j < N; j += 4) {
-        const float p = __builtin_amdgcn_exp2f(Ss[i * SP + j] - m_sub);
-        Ss[i * SP + j] = p;
-        sum += p;
+// Loads of n consecutive elements (n = 4 or 8) starting at element e,
+// widened to fp32. bf16 -> fp32 is exact (the bf16 bits are the top half).
+template <bool BF16, int NE>
+__device__ __forceinline__ void load_row_part(const void* base, size_t e, float* x) {
+  if (BF16) {
+    const uint16_t* p = (const uint16_t*)base + e;
+    if (NE == 4) {
+      const u32x2_t w = *(const u32x2_t*)p;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
       }
-    sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
-    if (i < M && part == 0) {
-      Rinv[i] = 1.0f / sum;
-      lse[bh * (size_t)M + i] = (mx + log2f(sum)) * kLn2;
-    }
-  }
-  __syncthreads();
-
-  // 4. O = P V / sum; each thread makes 4 consecutive d of one row.
-  const int dq = D / 4;
-  for (int idx = tid; idx < M * dq; idx += kSmallThreads) {
-    const int i = idx / dq, d0 = (idx - (idx / dq) * dq) * 4;
-    const float* pr = Ss + i * SP;
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-    const int jn = causal ? min(i + 1, N) : N;
-    for (int j = 0; j < jn; ++j) {
-      const float p = pr[j];
-      const float* vr = Vs + j * XP + d0;
-      a0 = fmaf(p, vr[0], a0);
-      a1 = fmaf(p, vr[1], a1);
-      a2 = fmaf(p, vr[2], a2);
-      a3 = fmaf(p, vr[3], a3);
-    }
-    const float r = Rinv[i];
-    const size_t at = q_off + (size_t)i * D + d0;
-    if (BF16) {
-      u32x2_t st;
-      st[0] = pack_bf16x2(a0 * r, a1 * r);
-      st[1] = pack_bf16x2(a2 * r, a3 * r);
-      *(u32x2_t*)((uint16_t*)ov + at) = st;
     } else {
-      const f32x4_t st = {a0 * r, a1 * r, a2 * r, a3 * r};
-      *(f32x4_t*)((float*)ov + at) = st;
+      const u32x4_t w = *(const u32x4_t*)p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float* p = (const float*)base + e;
+#pragma unroll
+    for (int i = 0; i < NE; i += 4) {
+      const f32x4_t w = *(const f32x4_t*)(p + i);
+      x[i] = w[0]; x[i + 1] = w[1]; x[i + 2] = w[2]; x[i + 3] = w[3];
     }
   }
 }
 
+template <bool BF16>
+__device__ __forceinline__ float load_one(const void* base, size_t e) {
+  if (BF16) return __uint_as_float((uint32_t)((const uint16_t*)base)[e] << 16);
+  return ((const float*)base)[e];
+}
+}  // namespace
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(kSmallQRows * 4 * 4) void attn_fwd_small_kernel(
+    const void* __restrict__ qv, const void* __restrict__ kv,
+    const void* __restrict__ vv, void* __restrict__ ov, float* __restrict__ lse,
+    int M, int N, int causal, float c) {
+  constexpr int DQ = D / 4;    // contraction elements per lane group in QK^T
+  constexpr int DB = D / 16;   // 16-wide d blocks of O
+  const int tid = workitem_id();
+  const int lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int q0 = (tid >> 6) * kSmallQRows;
+  const int qi = q0 + n;
+  const size_t bh = workgroup_id();
+  const size_t q_off = bh * (size_t)M * D;
+  const size_t kv_off = bh * (size_t)N * D;
+  // Key blocks this wave needs: all of them, or under the causal mask only
+  // those with a key <= the wave's last query.
+  const int n_vis = causal ? min(N, q0 + kSmallQRows) : N;
+  const int nkb = (n_vis + 15) >> 4;
+
+  // ---- all loads up front (rows past the end are clamped; their scores are
+  // masked, so the clamped values never reach the result).
+  float qf[DQ];
+  load_row_part<BF16, DQ>(qv, q_off + (size_t)min(qi, M - 1) * D + g * DQ, qf);
+  float kf[kSmallMaxKB][DQ];
+  float vf[kSmallMaxKB][DB][4];
+#pragma unroll
+  for (int kb = 0; kb < kSmallMaxKB; ++kb) {
+    if (kb < nkb) {
+      const int kr = min(16 * kb + n, N - 1);
+      load_row_part<BF16, DQ>(kv, kv_off + (size_t)kr * D + g * DQ, kf[kb]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int vr = min(16 * kb + 4 * g + r, N - 1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          vf[kb][db][r] = load_one<BF16>(vv, kv_off + (size_t)vr * D + 16 * db + n);
+      }
+    }
+  }
+
+  // ---- S^T = K Q^T, log2-domain scores, masks.
+  float s[kSmallMaxKB][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < kSmallMaxKB; ++kb) {
+    if (kb < nkb) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < DQ; ++t) acc = mfma_16x16x4_f32(kf[kb][t], qf[t], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * kb + 4 * g + r;
+        const bool masked = key >= N || (causal && key > qi);
+        s[kb][r] = masked ? -INFINITY : acc[r] * c;
+        mx = fmaxf(mx, s[kb][r]);
+      }
+    }
+  }
+  mx = half_pair_max(pair16_max(mx));
+  // Key 0 is visible to every row, so mx is finite for real rows; the guard
+  // keeps clamped tail rows free of inf - inf.
+  const float m_sub = mx == -INFINITY ? 0.0f : mx;
+
+  // ---- P = exp2(S - max), row sums, O^T = V^T P^T.
+  float l = 0.0f;
+  f32x4_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kb = 0; kb < kSmallMaxKB; ++kb) {
+    if (kb < nkb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_sub);
+        l += p;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma_16x16x4_f32(vf[kb][db][r], p, o[db]);
+      }
+    }
+  }
+  l = half_pair_sum(pair16_sum(l));
+
+  // ---- epilogue: O / l in the input dtype, L = ln 2 * (max + log2 l).
+  if (qi < M) {
+    const float rinv = 1.0f / l;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const size_t at = q_off + (size_t)qi * D + 16 * db + 4 * g;
+      if (BF16) {
+        u32x2_t st;
+        st[0] = pack_bf16x2(o[db][0] * rinv, o[db][1] * rinv);
+        st[1] = pack_bf16x2(o[db][2] * rinv, o[db][3] * rinv);
+        *(u32x2_t*)((uint16_t*)ov + at) = st;
+      } else {
+        const f32x4_t st = o[db] * rinv;
+        *(f32x4_t*)((float*)ov + at) = st;
+      }
+    }
+    if (g == 0) lse[bh * (size_t)M + qi] = (mx + log2f(l)) * kLn2;
+  }
+}
+
 hipError_t launch_small(const LaunchArgs& a, bool bf16) {
-  if (a.M > kSmallMaxM || a.N > kSmallMaxN || a.D > kSmallMaxD || a.D % 16)
+  if (a.M < 1 || a.M > kSmallMaxM || a.N < 1 || a.N > kSmallMaxN ||
+      (a.D != 16 && a.D != 32))
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)a.BH);
+  const dim3 block((unsigned)(64 * ((a.M + kSmallQRows - 1) / kSmallQRows)));
   const float c = a.scale * kLog2e;
-  if (bf16)
-    hipLaunchKernelGGL(attn_fwd_small_kernel<true>, grid, dim3(kSmallThreads), 0,
-                       a.stream, a.q, a.k, a.v, a.o, a.lse, (int)a.M, (int)a.N,
-                       (int)a.D, (int)a.causal, c);
-  else
-    hipLaunchKernelGGL(attn_fwd_small_kernel<false>, grid, dim3(kSmallThreads), 0,
-                       a.stream, a.q, a.k, a.v, a.o, a.lse, (int)a.M, (int)a.N,
-                       (int)a.D, (int)a.causal, c);
+  const int M = (int)a.M, N = (int)a.N, causal = (int)a.causal;
+#define MI355_SMALL_LAUNCH(BF, DD)                                                   \
+  hipLaunchKernelGGL((attn_fwd_small_kernel<BF, DD>), grid, block, 0, a.stream, a.q, \
+                     a.k, a.v, a.o, a.lse, M, N, causal, c)
+  if (bf16) {
+    if (a.D == 16) MI355_SMALL_LAUNCH(true, 16);
+    else MI355_SMALL_LAUNCH(true, 32);
+  } else {
+    if (a.D == 16) MI355_SMALL_LAUNCH(false, 16);
+    else MI355_SMALL_LAUNCH(false, 32);
+  }
+#undef MI355_SMALL_LAUNCH
   return hipGetLastError();
 }
 
