@@ -36,10 +36,16 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950",
 # canonicalising moves).
 KERNEL_FLAGS = ["-mno-amdgpu-ieee", "-fno-honor-nans"]
 
+# Per-source additions. The bf16 kernel keeps its MFMA accumulators in
+# architectural VGPRs (the vector ALU works on the score tiles directly, with
+# no accvgpr copies, and the whole wave fits in 256 registers: two
+# workgroups per CU).
+SOURCE_FLAGS = {"attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    extra = (KERNEL_FLAGS if src.endswith(".hip") else []) + SOURCE_FLAGS.get(src, [])
     cmd = [hipcc()] + COMMON + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -11,15 +11,18 @@
 // (key > query -> -inf), as in the Python reference.
 //
 // gfx950 mapping (not the pages' design):
-//  * One workgroup = 8 waves = 256 query rows of one (batch, head), two waves
-//    per SIMD. Key/value tiles of 64 rows stream HBM -> VGPRs -> LDS: the
-//    global loads of the next tile are issued at the start of an iteration
-//    and written to LDS at its end, one s_barrier per iteration.
-//  * Ping-pong between the two waves of a SIMD: waves 0-3 (group A) run
-//    S(j) = K(j) Q^T, softmax(j), O += V(j)^T P(j)^T in iteration j; waves
-//    4-7 (group B) run softmax(j-1), O += V(j-1)^T P(j-1)^T, S(j) = K(j) Q^T,
-//    carrying S(j) into the next iteration. While one wave of a SIMD is in
-//    its vector-ALU softmax the other keeps the matrix pipe busy.
+//  * One workgroup = 4 waves = 128 query rows of one (batch, head), one wave
+//    per SIMD; two workgroups share a CU. Key/value tiles of 64 rows stream
+//    HBM -> VGPRs -> LDS: the global loads of a tile are issued one
+//    iteration ahead and written to LDS at the end of the iteration, one
+//    s_barrier per iteration, double-buffered K and V rings.
+//  * Software pipeline inside each wave: iteration j computes
+//    S(j+1) = K(j+1) Q^T on the matrix cores while the vector ALU turns S(j)
+//    into probabilities P(j), then O += V(j)^T P(j)^T on the matrix cores
+//    while the vector ALU takes the row statistics of S(j+1). The two
+//    halves of each iteration are independent instruction streams, and
+//    sched_group_barrier interleaves them (one MFMA, then a few VALU and LDS
+//    instructions), so the softmax runs in the shadow of the MFMAs.
 //  * Both products run on v_mfma_f32_32x32x16_bf16 in transposed form,
 //    S^T = K Q^T and O^T += V^T P^T, so the accumulator column -- one query
 //    row -- belongs to lanes l and l^32: row max and row sum are in-register
@@ -59,18 +62,28 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
 // paths (masking, O rescale) stay off the per-tile instruction stream.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002;
+constexpr int kSgMfma = 0x008;
+constexpr int kSgVmemRead = 0x020;
+constexpr int kSgDsRead = 0x100;
+constexpr int kSgDsWrite = 0x200;
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format, no swizzle): loads past num_records return zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+#define MI355_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 }  // namespace
 
-// Waves per workgroup: two per SIMD, one of each ping-pong group.
-constexpr int kBf16Waves = 8;
+// Waves per workgroup: one per SIMD.
+constexpr int kBf16Waves = 4;
 
 template <int D, int WAVES>
 struct Bf16Cfg {
   static constexpr int NT = WAVES * 64;
   static constexpr int BM = WAVES * 32;
   static constexpr int BN = 64;                     // keys per tile
-  static constexpr int KBUF = 2;                    // K ring depth
-  static constexpr int VBUF = 3;                    // V ring depth (group B lags by one tile)
   static constexpr int ROWB = D * 2;                // bytes per key row
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
@@ -78,8 +91,10 @@ struct Bf16Cfg {
   static constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread
   static constexpr int QSTEPS = D / 16;
   static constexpr int DBLK = D < 32 ? 1 : D / 32;  // 32-row blocks of O^T
-  static constexpr int V_OFF = KBUF * TILEB;        // V ring after the K ring
-  static constexpr int ZERO_OFF = (KBUF + VBUF) * TILEB;  // 64 zero bytes after the rings
+  static constexpr int NF_QK = 2 * QSTEPS;          // MFMAs of one S tile
+  static constexpr int NF_PV = 4 * DBLK;            // MFMAs of one O update
+  static constexpr int V_OFF = 2 * TILEB;           // K ring (2), then V ring (2)
+  static constexpr int ZERO_OFF = 4 * TILEB;        // 64 zero bytes after the rings
   static constexpr int LDS_BYTES = ZERO_OFF + 64;
   // K row r of a tile holds key kperm(r); swizzles act on 16-byte chunks.
   __device__ static constexpr int kperm(int r) {
@@ -97,7 +112,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
     float* __restrict__ lse, int M, int N, int tiles_m, int n_wg, float c) {
   using C = Bf16Cfg<D, WAVES>;
   constexpr int NT = C::NT, BM = C::BM, BN = C::BN, ROWB = C::ROWB,
-                TILEB = C::TILEB, CPT = C::CPT, QSTEPS = C::QSTEPS, DBLK = C::DBLK;
+                TILEB = C::TILEB, CPT = C::CPT, QSTEPS = C::QSTEPS, DBLK = C::DBLK,
+                NF_QK = C::NF_QK, NF_PV = C::NF_PV;
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
 
@@ -121,14 +137,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
   const int q_wg0 = tm * BM;
   const int qw0 = q_wg0 + wave * 32;
   const int qi = qw0 + r32;  // this lane's query row
-  const bool wave_live = qw0 < M;
-  const int wave_last = min(qw0 + 31, M - 1);
 
+  // Key tiles the workgroup visits. Under the causal mask a wave may visit
+  // up to two tiles that are fully masked for its rows; they contribute
+  // exact zeros.
   int nt = (N + BN - 1) / BN;
   if (CAUSAL) nt = min(nt, (min(q_wg0 + BM, M) - 1) / BN + 1);
-  // tiles this wave computes: [0, wave_nt)
-  int wave_nt = 0;
-  if (wave_live) wave_nt = CAUSAL ? min(nt, wave_last / BN + 1) : nt;
 
   if (tid < 16) ((uint32_t*)(smem + C::ZERO_OFF))[tid] = 0u;
 
@@ -145,26 +159,25 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
     v_src[u] = R * D + (chp ^ C::swz_v(R)) * 8;
   }
   u32x4_t kst[CPT], vst[CPT];
-  const int tail_rows = N - (nt - 1) * BN;  // valid rows of the last tile
-  auto load_k = [&](int j) {
+  // Tile loads go through buffer descriptors bounded by the head's last key
+  // row: chunks past it read as zeros (finite, and masked or multiplied by
+  // p = 0), so the tail needs no per-lane clamp and tiles past the end need
+  // no guard. Offsets are per-lane constants; the tile base is scalar.
+  auto tile_rsrc = [&](const uint16_t* head, int j) {
     const int jc = min(j, nt - 1);
-    const uint16_t* base = kh + (size_t)jc * BN * D;
+    const uint32_t bytes = (uint32_t)(N - jc * BN) * (uint32_t)ROWB;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)jc * BN * D), (short)0,
+                                             (int)bytes, kBufferRsrcWord3);
+  };
+  auto load_k = [&](int j) {
+    const auto r = tile_rsrc(kh, j);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      int off = k_src[u];
-      if (jc == nt - 1 && off >= tail_rows * D) off = (tail_rows - 1) * D + (off & (D - 1));
-      kst[u] = *(const u32x4_t*)(base + off);
-    }
+    for (int u = 0; u < CPT; ++u) kst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * k_src[u], 0, 0);
   };
   auto load_v = [&](int j) {
-    const int jc = min(j, nt - 1);
-    const uint16_t* base = vh + (size_t)jc * BN * D;
+    const auto r = tile_rsrc(vh, j);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      int off = v_src[u];
-      if (jc == nt - 1 && off >= tail_rows * D) off = (tail_rows - 1) * D + (off & (D - 1));
-      vst[u] = *(const u32x4_t*)(base + off);
-    }
+    for (int u = 0; u < CPT; ++u) vst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * v_src[u], 0, 0);
   };
   auto store_k = [&](int buf) {
 #pragma unroll
@@ -207,40 +220,29 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
 
   const float cc_scale = POS_SCALE ? c : 1.0f;
   float m_run = -INFINITY;  // reference max, log2 domain
+  float m_sub = 0.0f;       // exponent offset of the tile being exponentiated
   float l_run = 0.0f;       // this lane's part of the row sum (of bf16 P)
   f32x16_t acc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
-  f32x16_t s_cur[2];  // scores of the tile in flight
+  f32x16_t s_a[2], s_b[2];  // scores of two consecutive tiles
 
-  // Operand fragments are read from LDS PF MFMAs ahead of their use (a ring
-  // of PF+1 register fragments), and consecutive MFMAs go to independent
-  // accumulators, so LDS latency overlaps matrix work.
-  constexpr int PF = 3;
-
-  // S^T = K Q^T for the 64-key tile in buffer buf: fragment i is key block
-  // kb = i & 1 at d-step t = i >> 1.
+  // S^T = K Q^T for the 64-key tile in K buffer buf: fragment i is key
+  // block kb = i & 1 at d-step t = i >> 1.
   auto qk = [&](int buf, f32x16_t* s) {
     const unsigned char* kb_base = smem + buf * TILEB + k_rd;
-    constexpr int NF = 2 * QSTEPS;
-    auto frag = [&](int i) -> u32x4_t {
-      const int t = i >> 1, kb = i & 1;
-      return *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
-    };
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-    u32x4_t fr[PF + 1];
 #pragma unroll
-    for (int i = 0; i < PF && i < NF; ++i) fr[i] = frag(i);
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      if (i + PF < NF) fr[(i + PF) % (PF + 1)] = frag(i + PF);
-      s[i & 1] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (PF + 1)]), qf[i >> 1],
-                                    s[i & 1]);
+    for (int i = 0; i < NF_QK; ++i) {
+      const int t = i >> 1, kb = i & 1;
+      const u32x4_t fr =
+          *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
+      s[kb] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr), qf[t], s[kb]);
     }
   };
 
@@ -249,55 +251,51 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
   auto pv = [&](int buf, const u32x4_t (*p)[2]) {
     const unsigned char* vb_base = smem + C::V_OFF + buf * TILEB;
     const unsigned char* zero = smem + C::ZERO_OFF;
-    constexpr int NF = 4 * DBLK;
     typedef __attribute__((ext_vector_type(8))) short s16x8_t;
-    auto frag = [&](int i) -> s16x8_t {
+#pragma unroll
+    for (int i = 0; i < NF_PV; ++i) {
       const int b = i % DBLK, kt = i / DBLK, kb = kt >> 1, t = kt & 1;
       const int row_off = (kb * 32 + t * 8) * ROWB;
       const unsigned char* a0 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off;
       const unsigned char* a1 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off + 4 * ROWB;
       const s16x4_t lo = lds_read_tr16(a0);
       const s16x4_t hi = lds_read_tr16(a1);
-      return (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    s16x8_t fr[PF + 1];
-#pragma unroll
-    for (int i = 0; i < PF && i < NF; ++i) fr[i] = frag(i);
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      if (i + PF < NF) fr[(i + PF) % (PF + 1)] = frag(i + PF);
-      const int b = i % DBLK, kt = i / DBLK;
-      acc[b] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (PF + 1)]),
-                                  __builtin_bit_cast(bf16x8_t, p[kt >> 1][kt & 1]), acc[b]);
+      const s16x8_t fr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[b] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr),
+                                  __builtin_bit_cast(bf16x8_t, p[kb][t]), acc[b]);
     }
   };
 
-  // Row statistics of a fresh score tile: scale (negative / zero scale),
-  // mask (causal diagonal, key tail), tile max, and the lazy reference
-  // update. Produces the exponent offset for this tile and whether O and l
-  // must be rescaled (by alpha) before its probabilities are added.
-  struct TileStats {
-    float m_sub;
-    float alpha;
-    bool resc;
+  // Scale (negative / zero scale only) and mask (causal diagonal, key tail)
+  // a fresh score tile. Only tiles that need it go through the mask.
+  auto needs_mask = [&](int j) {
+    const int key0 = j * BN;
+    return (key0 + BN > N) || (CAUSAL && key0 + BN - 1 > qw0);
   };
-  auto tile_stats = [&](f32x16_t* s, int key0, bool mask) -> TileStats {
+  auto scale_tile = [&](f32x16_t* s) {
     if (!POS_SCALE) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] *= c;
     }
-    if (mask) {
-      keep_branch();
+  };
+  auto mask_tile = [&](f32x16_t* s, int j) {
+    const int key0 = j * BN;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kb * 32 + g * 16 + i;
-          if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + kb * 32 + g * 16 + i;
+        if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
+      }
+  };
+
+  // Row statistics of a prepared score tile: tile max and the lazy
+  // reference update. Sets m_sub for the tile's exponentials; returns
+  // whether O and l must be rescaled by alpha before its probabilities are
+  // added.
+  auto stats = [&](const f32x16_t* s, float& alpha) -> bool {
     float mx = __builtin_fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -306,18 +304,17 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
         mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[kb][i], s[kb][i + 1]));
     mx = half_pair_max(mx);
     const float m_cand = __builtin_fmaxf(m_run, mx * cc_scale);
-    TileStats st;
-    st.resc = wave_any(m_cand > m_run + kRescaleThreshold);
-    const float m_new = st.resc ? m_cand : m_run;
-    st.m_sub = (m_new == -INFINITY) ? 0.0f : m_new;
-    st.alpha = __builtin_amdgcn_exp2f(m_run - st.m_sub);
+    const bool resc = wave_any(m_cand > m_run + kRescaleThreshold);
+    const float m_new = resc ? m_cand : m_run;
+    m_sub = (m_new == -INFINITY) ? 0.0f : m_new;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
     m_run = m_new;
-    return st;
+    return resc;
   };
 
   // Probabilities of one 32-key half of a tile: bf16 P (B-operand layout)
   // and their row sum (of the rounded values, via v_dot2_f32_bf16 with 1s).
-  auto tile_exp = [&](const f32x16_t& s, float m_sub, u32x4_t* p) -> float {
+  auto tile_exp = [&](const f32x16_t& s, u32x4_t* p) -> float {
     // The row sum is accumulated from each freshly rounded bf16 pair (not
     // from elements extracted back out of the packed vector).
     const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -346,65 +343,118 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
       for (int i = 0; i < 16; ++i) acc[b][i] *= a;
   };
 
-  auto needs_mask = [&](int j) {
-    const int key0 = j * BN;
-    return (key0 + BN > N) || (CAUSAL && key0 + BN - 1 > qw0);
-  };
-
-  // P(j) from S(j) with its stats, the l update and the O rescale (O holds
-  // tiles < j at the previous reference); then O += V(j)^T P(j)^T.
-  auto softmax_pv = [&](f32x16_t* s, int j) {
-    const TileStats st = tile_stats(s, j * BN, needs_mask(j));
-    u32x4_t p[2][2];
-    float rs = tile_exp(s[0], st.m_sub, p[0]);
-    rs += tile_exp(s[1], st.m_sub, p[1]);
-    l_run = (st.resc ? l_run * st.alpha : l_run) + rs;
-    if (st.resc) {
-      keep_branch();
-      rescale(st.alpha);
+  // Instruction interleave of the first half of an iteration: the S(j+1)
+  // MFMAs with their K reads, the exponentials of S(j), and the global
+  // loads of the tiles after next.
+  auto sched_a = [&]() {
+    constexpr int VALU = (96 + NF_QK - 1) / NF_QK;
+    constexpr int VMEM = 2 * CPT;
+    MI355_SCHED(kSgDsRead, 2);
+#pragma unroll
+    for (int i = 0; i < NF_QK; ++i) {
+      MI355_SCHED(kSgMfma, 1);
+      if (i + 2 < NF_QK) MI355_SCHED(kSgDsRead, 1);
+      if (i < VMEM) MI355_SCHED(kSgVmemRead, 1);
+      MI355_SCHED(kSgValu, VALU);
     }
-    pv(j % C::VBUF, p);
+  };
+  // Second half: the O MFMAs with their V^T reads, the statistics of
+  // S(j+1), and the LDS writes of the staged tiles at the end.
+  auto sched_b = [&]() {
+    MI355_SCHED(kSgDsRead, 4);
+#pragma unroll
+    for (int i = 0; i < NF_PV; ++i) {
+      MI355_SCHED(kSgMfma, 1);
+      if (2 * i + 4 < 2 * NF_PV) MI355_SCHED(kSgDsRead, 2);
+      MI355_SCHED(kSgValu, 3);
+    }
+    MI355_SCHED(kSgDsWrite, 2 * CPT);
   };
 
-  const bool group_b = wave >= WAVES / 2;
+  // One iteration: tile j is exponentiated and added to O; with a next
+  // tile, S(j+1) is computed alongside and its statistics taken, and the
+  // tiles K(j+2), V(j+1) are staged into the buffers freed one iteration
+  // ago. MASKED: tile j+1 may need the causal / tail mask (a few tiles per
+  // workgroup); the common unmasked step has no branch between its halves,
+  // so the interleave spans the whole iteration.
+  auto step = [&](int j, f32x16_t* sc, f32x16_t* sn, bool has_next, bool masked) {
+    if (has_next) {
+      load_k(j + 2);
+      load_v(j + 1);
+      qk((j + 1) & 1, sn);
+    }
+    u32x4_t p[2][2];
+    float rs = tile_exp(sc[0], p[0]);
+    rs += tile_exp(sc[1], p[1]);
+    if (has_next && !masked) sched_a();
+    l_run += rs;
+    if (has_next) {
+      scale_tile(sn);
+      if (masked && needs_mask(j + 1)) {
+        keep_branch();
+        mask_tile(sn, j + 1);
+      }
+    }
+    pv(j & 1, p);
+    if (has_next) {
+      float alpha;
+      const bool resc = stats(sn, alpha);
+      store_k(j & 1);
+      store_v((j + 1) & 1);
+      if (!masked) sched_b();
+      if (resc) {
+        keep_branch();
+        rescale(alpha);
+        l_run *= alpha;
+      }
+      __syncthreads();
+    }
+  };
 
-  // ---- prologue: K(0), V(0) -> LDS.
+  // ---- prologue: K(0), K(1), V(0) -> LDS; S(0) and its statistics.
   load_k(0);
   load_v(0);
   store_k(0);
   store_v(0);
-  __syncthreads();  // K(0), V(0) and the zero block visible
-
-  // The two groups run separate copies of the loop (same barrier count) so
-  // that each copy is register-allocated for its own live ranges.
-  if (!group_b) {
-    for (int j = 0; j < nt; ++j) {
-      load_k(j + 1);
-      load_v(j + 1);
-      if (j < wave_nt) {
-        qk(j & 1, s_cur);
-        softmax_pv(s_cur, j);
-      }
-      // every wave is past its reads of K(j-1) [buffer (j+1)&1] and of
-      // V(j-2) [buffer (j+1)%3]: overwrite them with K(j+1) and V(j+1).
-      store_k((j + 1) & 1);
-      store_v((j + 1) % C::VBUF);
-      __syncthreads();
-    }
-  } else {
-    for (int j = 0; j < nt; ++j) {
-      load_k(j + 1);
-      load_v(j + 1);
-      if (j >= 1 && j - 1 < wave_nt) softmax_pv(s_cur, j - 1);
-      if (j < wave_nt) qk(j & 1, s_cur);
-      store_k((j + 1) & 1);
-      store_v((j + 1) % C::VBUF);
-      __syncthreads();
-    }
-    if (nt - 1 < wave_nt) softmax_pv(s_cur, nt - 1);
+  load_k(1);
+  store_k(1);
+  __syncthreads();  // K(0), K(1), V(0) and the zero block visible
+  qk(0, s_a);
+  scale_tile(s_a);
+  if (needs_mask(0)) {
+    keep_branch();
+    mask_tile(s_a, 0);
   }
+  {
+    float alpha;
+    stats(s_a, alpha);  // O and l are still zero: nothing to rescale
+  }
+  __syncthreads();  // every wave is done with K(0) before step 0 restages its buffer
 
-  if (!wave_live) return;
+  // Steps j < jf have an unmasked tile j+1 (for every wave of the group);
+  // the rest run the masked variant. The current tile is in s_a at the
+  // start of each loop.
+  int j_free = N / BN;  // tiles without a key tail
+  if (CAUSAL) j_free = min(j_free, (q_wg0 + 1) / BN);  // below the diagonal for all rows
+  const int jf = max(0, min(nt - 1, j_free - 1));
+  int j = 0;
+  for (; j + 1 < jf; j += 2) {
+    step(j, s_a, s_b, true, false);
+    step(j + 1, s_b, s_a, true, false);
+  }
+  if (j < jf) {
+    step(j, s_a, s_b, true, false);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_a[kb] = s_b[kb];
+    ++j;
+  }
+  for (; j + 1 < nt; ++j) {
+    step(j, s_a, s_b, true, true);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_a[kb] = s_b[kb];
+  }
+  step(nt - 1, s_a, s_b, false, false);
+
   const float l_tot = half_pair_sum(l_run);
   if (qi >= M) return;
   const float inv = 1.0f / l_tot;
