@@ -13,16 +13,23 @@
 // gfx950 mapping (not the pages' design):
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head), one wave
 //    per SIMD; two workgroups share a CU. Key/value tiles of 64 rows stream
-//    HBM -> VGPRs -> LDS: the global loads of a tile are issued one
-//    iteration ahead and written to LDS at the end of the iteration, one
-//    s_barrier per iteration, double-buffered K and V rings.
-//  * Software pipeline inside each wave: iteration j computes
-//    S(j+1) = K(j+1) Q^T on the matrix cores while the vector ALU turns S(j)
-//    into probabilities P(j), then O += V(j)^T P(j)^T on the matrix cores
-//    while the vector ALU takes the row statistics of S(j+1). The two
-//    halves of each iteration are independent instruction streams, and
-//    sched_group_barrier interleaves them (one MFMA, then a few VALU and LDS
-//    instructions), so the softmax runs in the shadow of the MFMAs.
+//    HBM -> VGPRs -> LDS through bounded buffer loads, written to LDS half an
+//    iteration after they are issued (K in the first half, V in the second);
+//    rings of 3 K and 2 V tiles, one s_barrier per iteration.
+//  * Software pipeline inside each wave: iteration j runs S(j+1) =
+//    K(j+1) Q^T on the matrix cores while the vector ALU turns S(j) into
+//    P(j), then O += V(j)^T P(j)^T, whose MFMAs need almost no vector work,
+//    so the two waves of a SIMD overlap one's exponentials with the other's
+//    products. sched_group_barrier interleaves each half (one MFMA, then a
+//    few VALU and LDS instructions).
+//  * The common tile needs no row max. After the first tile sets the
+//    reference m to its exact row max, a tile is exponentiated against the
+//    current m; every p is >= 0, so a lane's partial row sum bounds each of
+//    its p. Only when that sum exceeds 2^16 (some score rose more than ~11
+//    above m, in log2 units) does the tile take the exact path: S recomputed
+//    from the K tile still in LDS, row max, new m, O and l rescaled, P
+//    recomputed. The reference therefore moves rarely and never lets p or
+//    the fp32 sums approach overflow.
 //  * Both products run on v_mfma_f32_32x32x16_bf16 in transposed form,
 //    S^T = K Q^T and O^T += V^T P^T, so the accumulator column -- one query
 //    row -- belongs to lanes l and l^32: row max and row sum are in-register
@@ -38,8 +45,6 @@
 //    operand reads of a half-wave hit distinct LDS banks.
 //  * Row sums are taken from the bf16-rounded P with v_dot2_f32_bf16, so l
 //    and the second product see the same probabilities.
-//  * The running max is moved lazily (only when a row max grows by more than
-//    2^8), so most tiles skip the O rescale.
 //  * Workgroup ids are renumbered so that the query tiles of one head land on
 //    one XCD and share its L2 for K/V; causal grids run heavy tiles first.
 
@@ -93,9 +98,13 @@ struct Bf16Cfg {
   static constexpr int DBLK = D < 32 ? 1 : D / 32;  // 32-row blocks of O^T
   static constexpr int NF_QK = 2 * QSTEPS;          // MFMAs of one S tile
   static constexpr int NF_PV = 4 * DBLK;            // MFMAs of one O update
-  static constexpr int V_OFF = 2 * TILEB;           // K ring (2), then V ring (2)
-  static constexpr int ZERO_OFF = 4 * TILEB;        // 64 zero bytes after the rings
-  static constexpr int LDS_BYTES = ZERO_OFF + 64;
+  static constexpr int KBUF = 3;                    // K ring depth
+  static constexpr int VBUF = 2;                    // V ring depth
+  static constexpr int V_OFF = KBUF * TILEB;        // K ring, then V ring
+  // 64 zero bytes after the rings, read in place of V^T columns past the
+  // head (only D = 16 has any); without them two workgroups fit a CU's LDS.
+  static constexpr int ZERO_OFF = (KBUF + VBUF) * TILEB;
+  static constexpr int LDS_BYTES = ZERO_OFF + (D < 32 ? 64 : 0);
   // K row r of a tile holds key kperm(r); swizzles act on 16-byte chunks.
   __device__ static constexpr int kperm(int r) {
     const int b = r & 31;
@@ -106,7 +115,7 @@ struct Bf16Cfg {
 };
 
 template <int D, int WAVES, bool CAUSAL, bool POS_SCALE>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int M, int N, int tiles_m, int n_wg, float c) {
@@ -144,20 +153,25 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
   int nt = (N + BN - 1) / BN;
   if (CAUSAL) nt = min(nt, (min(q_wg0 + BM, M) - 1) / BN + 1);
 
-  if (tid < 16) ((uint32_t*)(smem + C::ZERO_OFF))[tid] = 0u;
+  if (D < 32 && tid < 16) ((uint32_t*)(smem + C::ZERO_OFF))[tid] = 0u;
 
   // ---- staging geometry: thread chunk u is LDS chunk ch = tid + u*NT of a
-  // tile, i.e. row ch / CPR at swizzled position ch % CPR.
-  int k_src[CPT], v_src[CPT], dst[CPT];
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    int ch = tid + u * NT;
-    if (ch >= C::CHUNKS) ch = C::CHUNKS - 1;  // surplus threads repeat the last chunk
-    const int R = ch / C::CPR, chp = ch % C::CPR;
-    dst[u] = R * ROWB + chp * 16;
-    k_src[u] = C::kperm(R) * D + (chp ^ C::swz_k(R)) * 8;  // elements from the tile's first key
-    v_src[u] = R * D + (chp ^ C::swz_v(R)) * 8;
-  }
+  // tile, i.e. row ch / CPR at swizzled position ch % CPR. Chunk u sits
+  // RPU = NT / CPR rows below chunk 0 with the same column, and kperm and
+  // the swizzles act on the low row bits only (a bit permutation of bits
+  // 0-4, and bits 0-3), so every per-chunk offset is chunk 0's plus a
+  // compile-time constant: one base register per tensor.
+  constexpr int RPU = NT / C::CPR;
+  int ch0 = tid;
+  if (ch0 >= C::CHUNKS) ch0 = C::CHUNKS - 1;  // surplus threads repeat the last chunk
+  const int R0 = ch0 / C::CPR, chp0 = ch0 % C::CPR;
+  const int dst0 = R0 * ROWB + chp0 * 16;
+  const int k_src0 = 2 * (C::kperm(R0) * D + (chp0 ^ C::swz_k(R0)) * 8);  // bytes from the tile's first key
+  const int v_src0 = 2 * (R0 * D + (chp0 ^ C::swz_v(R0)) * 8);
+  auto dst_off = [&](int u) { return u * NT * 16; };
+  auto k_src_off = [&](int u) { return 2 * C::kperm(u * RPU) * D; };
+  auto v_src_off = [&](int u) { return 2 * u * RPU * D; };
+  static_assert(CPT == 1 || RPU >= 16, "per-chunk offsets need the row bits of chunk 0 below RPU");
   u32x4_t kst[CPT], vst[CPT];
   // Tile loads go through buffer descriptors bounded by the head's last key
   // row: chunks past it read as zeros (finite, and masked or multiplied by
@@ -172,20 +186,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
   auto load_k = [&](int j) {
     const auto r = tile_rsrc(kh, j);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) kst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * k_src[u], 0, 0);
+    for (int u = 0; u < CPT; ++u)
+      kst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, k_src0 + k_src_off(u), 0, 0);
   };
   auto load_v = [&](int j) {
     const auto r = tile_rsrc(vh, j);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) vst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, 2 * v_src[u], 0, 0);
+    for (int u = 0; u < CPT; ++u)
+      vst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, v_src0 + v_src_off(u), 0, 0);
   };
   auto store_k = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) *(u32x4_t*)(smem + buf * TILEB + dst[u]) = kst[u];
+    for (int u = 0; u < CPT; ++u) *(u32x4_t*)(smem + buf * TILEB + dst0 + dst_off(u)) = kst[u];
   };
   auto store_v = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) *(u32x4_t*)(smem + C::V_OFF + buf * TILEB + dst[u]) = vst[u];
+    for (int u = 0; u < CPT; ++u)
+      *(u32x4_t*)(smem + C::V_OFF + buf * TILEB + dst0 + dst_off(u)) = vst[u];
   };
 
   // ---- per-lane operand read offsets (bytes within a tile)
@@ -291,11 +308,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
       }
   };
 
-  // Row statistics of a prepared score tile: tile max and the lazy
-  // reference update. Sets m_sub for the tile's exponentials; returns
-  // whether O and l must be rescaled by alpha before its probabilities are
-  // added.
-  auto stats = [&](const f32x16_t* s, float& alpha) -> bool {
+  // Exact reference update for a prepared score tile (prologue and the
+  // rare overflow path): m becomes max(m, row max); returns the factor for
+  // O and l.
+  auto exact_ref = [&](const f32x16_t* s) -> float {
     float mx = __builtin_fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -303,13 +319,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
       for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2)
         mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[kb][i], s[kb][i + 1]));
     mx = half_pair_max(mx);
-    const float m_cand = __builtin_fmaxf(m_run, mx * cc_scale);
-    const bool resc = wave_any(m_cand > m_run + kRescaleThreshold);
-    const float m_new = resc ? m_cand : m_run;
-    m_sub = (m_new == -INFINITY) ? 0.0f : m_new;
-    alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
+    const float m_new = __builtin_fmaxf(m_run, mx * cc_scale);
+    const float m_new_sub = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_sub - m_new_sub);
     m_run = m_new;
-    return resc;
+    m_sub = m_new_sub;
+    return alpha;
   };
 
   // Probabilities of one 32-key half of a tile: bf16 P (B-operand layout)
@@ -343,81 +358,141 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
       for (int i = 0; i < 16; ++i) acc[b][i] *= a;
   };
 
-  // Instruction interleave of the first half of an iteration: the S(j+1)
-  // MFMAs with their K reads, the exponentials of S(j), and the global
-  // loads of the tiles after next.
-  auto sched_a = [&]() {
-    constexpr int VALU = (96 + NF_QK - 1) / NF_QK;
-    constexpr int VMEM = 2 * CPT;
-    MI355_SCHED(kSgDsRead, 2);
-#pragma unroll
-    for (int i = 0; i < NF_QK; ++i) {
-      MI355_SCHED(kSgMfma, 1);
-      if (i + 2 < NF_QK) MI355_SCHED(kSgDsRead, 1);
-      if (i < VMEM) MI355_SCHED(kSgVmemRead, 1);
-      MI355_SCHED(kSgValu, VALU);
-    }
+  // K fragment i of the S^T product (key block i & 1, d-step i >> 1) and V^T
+  // fragment i of the O^T product (O block i % DBLK, key step i / DBLK).
+  typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+  auto k_frag = [&](const unsigned char* kb_base, int i) -> u32x4_t {
+    const int t = i >> 1, kb = i & 1;
+    return *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
   };
-  // Second half: the O MFMAs with their V^T reads, the statistics of
-  // S(j+1), and the LDS writes of the staged tiles at the end.
-  auto sched_b = [&]() {
-    MI355_SCHED(kSgDsRead, 4);
-#pragma unroll
-    for (int i = 0; i < NF_PV; ++i) {
-      MI355_SCHED(kSgMfma, 1);
-      if (2 * i + 4 < 2 * NF_PV) MI355_SCHED(kSgDsRead, 2);
-      MI355_SCHED(kSgValu, 3);
-    }
-    MI355_SCHED(kSgDsWrite, 2 * CPT);
+  auto v_frag = [&](const unsigned char* vb_base, int i) -> s16x8_t {
+    const unsigned char* zero = smem + C::ZERO_OFF;
+    const int b = i % DBLK, kt = i / DBLK, kb = kt >> 1, t = kt & 1;
+    const int row_off = (kb * 32 + t * 8) * ROWB;
+    const unsigned char* a0 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off;
+    const unsigned char* a1 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off + 4 * ROWB;
+    const s16x4_t lo = lds_read_tr16(a0);
+    const s16x4_t hi = lds_read_tr16(a1);
+    return (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
-  // One iteration: tile j is exponentiated and added to O; with a next
-  // tile, S(j+1) is computed alongside and its statistics taken, and the
-  // tiles K(j+2), V(j+1) are staged into the buffers freed one iteration
-  // ago. MASKED: tile j+1 may need the causal / tail mask (a few tiles per
-  // workgroup); the common unmasked step has no branch between its halves,
-  // so the interleave spans the whole iteration.
-  auto step = [&](int j, f32x16_t* sc, f32x16_t* sn, bool has_next, bool masked) {
-    if (has_next) {
-      load_k(j + 2);
-      load_v(j + 1);
-      qk((j + 1) & 1, sn);
+  // Operand fragments are read KPF / VPF chunks ahead of their MFMA.
+  constexpr int KPF = 3, VPF = 3;
+
+  // First half of an iteration, as NF_QK fenced chunks: each issues the K
+  // fragment read KPF chunks ahead, one S(j+1) MFMA, a share of the
+  // exponentials of S(j) (two at a time: fma, exp2, round to bf16, row sum)
+  // and, in the first chunks, the global loads of K(j+2). The fences
+  // (sched_barrier) fix the chunk order; inside a chunk the scheduler is
+  // free. Returns the lane's partial row sum of P(j).
+  auto region_a = [&](int j, const f32x16_t* sc, f32x16_t* sn, u32x4_t (*p)[2])
+                      __attribute__((always_inline)) -> float {
+    constexpr int PPC = 16 / NF_QK;  // exponential pairs per chunk
+    const unsigned char* kb_base = smem + ((j + 1) % C::KBUF) * TILEB + k_rd;
+    const auto rk = tile_rsrc(kh, j + 2);
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[kb][i] = 0.0f;
+    u32x4_t fr[KPF + 1];
+#pragma unroll
+    for (int i = 0; i < KPF && i < NF_QK; ++i) fr[i] = k_frag(kb_base, i);
+    float rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NF_QK; ++i) {
+      if (i + KPF < NF_QK) fr[(i + KPF) % (KPF + 1)] = k_frag(kb_base, i + KPF);
+      if (i < CPT) kst[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_src0 + k_src_off(i), 0, 0);
+#pragma unroll
+      for (int q = 0; q < PPC; ++q) {
+        const int pr = i * PPC + q, kb = pr >> 3, t = (pr >> 2) & 1, e = pr & 3;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][t * 8 + 2 * e], cc_scale, -m_sub));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][t * 8 + 2 * e + 1], cc_scale, -m_sub));
+        const f32x2_t f = {p0, p1};
+        const bf16x2_t bb = __builtin_convertvector(f, bf16x2_t);
+        p[kb][t][e] = __builtin_bit_cast(uint32_t, bb);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(bb, one, rs, false);
+      }
+      // the vector work of the chunk is issued before the MFMA's operand
+      // wait, so an LDS stall does not hold it back
+      __builtin_amdgcn_sched_barrier(0);
+      sn[i & 1] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (KPF + 1)]), qf[i >> 1],
+                                     sn[i & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    return rs;
+  };
+
+  // Second half, as NF_PV fenced chunks: the V^T fragment reads VPF chunks
+  // ahead, one O MFMA each and, with a next tile, the loads of V(j+1).
+  auto region_b = [&](int j, const u32x4_t (*p)[2], bool has_next) __attribute__((always_inline)) {
+    const unsigned char* vb_base = smem + C::V_OFF + (j & 1) * TILEB;
+    const auto rv = tile_rsrc(vh, j + 1);
+    s16x8_t fr[VPF + 1];
+#pragma unroll
+    for (int i = 0; i < VPF && i < NF_PV; ++i) fr[i] = v_frag(vb_base, i);
+#pragma unroll
+    for (int i = 0; i < NF_PV; ++i) {
+      if (i + VPF < NF_PV) fr[(i + VPF) % (VPF + 1)] = v_frag(vb_base, i + VPF);
+      if (has_next && i < CPT)
+        vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_src0 + v_src_off(i), 0, 0);
+      const int b = i % DBLK, kt = i / DBLK;
+      acc[b] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (VPF + 1)]),
+                                  __builtin_bit_cast(bf16x8_t, p[kt >> 1][kt & 1]), acc[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (has_next && NF_PV < CPT) load_v(j + 1);  // (never: NF_PV >= CPT for every D)
+  };
+
+  // Row-sum bound that sends a tile to the exact path: a lane's partial sum
+  // of p over its 32 keys; any single p above 2^16 / 32 trips it.
+  constexpr float kRowSumLimit = 65536.0f;
+
+  // Iteration j: P(j) from S(j) (against the current reference) and
+  // O += V(j)^T P(j)^T; with a next tile, S(j+1) = K(j+1) Q^T alongside, its
+  // scale and mask, and the staging of K(j+2), V(j+1) into the ring slots
+  // freed one iteration ago.
+  auto iter = [&](int j, f32x16_t* sc, f32x16_t* sn, bool has_next) __attribute__((always_inline)) {
     u32x4_t p[2][2];
-    float rs = tile_exp(sc[0], p[0]);
-    rs += tile_exp(sc[1], p[1]);
-    if (has_next && !masked) sched_a();
-    l_run += rs;
+    float rs;
     if (has_next) {
+      rs = region_a(j, sc, sn, p);
+      store_k((j + 2) % C::KBUF);
+    } else {
+      rs = tile_exp(sc[0], p[0]) + tile_exp(sc[1], p[1]);
+    }
+    if (wave_any(rs > kRowSumLimit)) {
+      // Some score rose far above the reference: redo this tile exactly
+      // (O holds tiles < j; K(j) is still in its ring slot).
+      keep_branch();
+      qk(j % C::KBUF, sc);
+      scale_tile(sc);
+      if (needs_mask(j)) mask_tile(sc, j);
+      const float alpha = exact_ref(sc);
+      rescale(alpha);
+      l_run *= alpha;
+      rs = tile_exp(sc[0], p[0]) + tile_exp(sc[1], p[1]);
+    }
+    l_run += rs;
+    region_b(j, p, has_next);
+    if (has_next) {
+      store_v((j + 1) & 1);
       scale_tile(sn);
-      if (masked && needs_mask(j + 1)) {
+      if (needs_mask(j + 1)) {
         keep_branch();
         mask_tile(sn, j + 1);
-      }
-    }
-    pv(j & 1, p);
-    if (has_next) {
-      float alpha;
-      const bool resc = stats(sn, alpha);
-      store_k(j & 1);
-      store_v((j + 1) & 1);
-      if (!masked) sched_b();
-      if (resc) {
-        keep_branch();
-        rescale(alpha);
-        l_run *= alpha;
       }
       __syncthreads();
     }
   };
 
-  // ---- prologue: K(0), K(1), V(0) -> LDS; S(0) and its statistics.
+  // ---- prologue: K(0), K(1), V(0) -> LDS; S(0) and its exact reference.
   load_k(0);
-  load_v(0);
   store_k(0);
-  store_v(0);
   load_k(1);
   store_k(1);
+  load_v(0);
+  store_v(0);
   __syncthreads();  // K(0), K(1), V(0) and the zero block visible
   qk(0, s_a);
   scale_tile(s_a);
@@ -425,35 +500,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(
     keep_branch();
     mask_tile(s_a, 0);
   }
-  {
-    float alpha;
-    stats(s_a, alpha);  // O and l are still zero: nothing to rescale
-  }
-  __syncthreads();  // every wave is done with K(0) before step 0 restages its buffer
+  exact_ref(s_a);  // O and l are still zero: nothing to rescale
 
-  // Steps j < jf have an unmasked tile j+1 (for every wave of the group);
-  // the rest run the masked variant. The current tile is in s_a at the
-  // start of each loop.
-  int j_free = N / BN;  // tiles without a key tail
-  if (CAUSAL) j_free = min(j_free, (q_wg0 + 1) / BN);  // below the diagonal for all rows
-  const int jf = max(0, min(nt - 1, j_free - 1));
+  // Iteration j keeps S(j) in s_a (j even) or s_b (j odd).
   int j = 0;
-  for (; j + 1 < jf; j += 2) {
-    step(j, s_a, s_b, true, false);
-    step(j + 1, s_b, s_a, true, false);
+  for (; j + 2 < nt; j += 2) {
+    iter(j, s_a, s_b, true);
+    iter(j + 1, s_b, s_a, true);
   }
-  if (j < jf) {
-    step(j, s_a, s_b, true, false);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_a[kb] = s_b[kb];
-    ++j;
+  if (j + 1 < nt) {
+    iter(j, s_a, s_b, true);
+    iter(j + 1, s_b, s_a, false);
+  } else {
+    iter(j, s_a, s_b, false);
   }
-  for (; j + 1 < nt; ++j) {
-    step(j, s_a, s_b, true, true);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_a[kb] = s_b[kb];
-  }
-  step(nt - 1, s_a, s_b, false, false);
 
   const float l_tot = half_pair_sum(l_run);
   if (qi >= M) return;

@@ -110,6 +110,27 @@ def test_constant_v_and_causal_row0(dtype):
     assert np.abs(lse[:, :, 0] - ref_l0).max() <= TOL[dtype][1]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_move_the_reference(dtype, causal):
+    """Scores that climb by ~12 (natural-log units) every 64 keys, plus one
+    key whose score overflows exp2 against the running reference: the
+    reference max has to move on almost every tile (the kernels' rescale
+    paths), including a jump past the fp32 exponent range."""
+    B, H, M, N, D = 1, 2, 96, 640, 64
+    g = torch.Generator().manual_seed(47)
+    u = torch.zeros(D)
+    u[0] = 1.0
+    q = torch.randn(B, H, M, D, generator=g) * 0.5 + 2.0 * u
+    ramp = torch.arange(N, dtype=torch.float32) * (6.0 / 64.0)
+    k = torch.randn(B, H, N, D, generator=g) * 0.5 + ramp[:, None] * u
+    k[:, :, 500] = 90.0 * u  # score ~180: 2^(260) relative to earlier rows
+    v = torch.randn(B, H, N, D, generator=g)
+    if dtype == "bf16":
+        q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    check_full(q, k, v, causal, 1.0, label="rising", magnitude_tol=True)
+
+
 def test_key_shift_invariance_fp32():
     """Adding u to every key adds scale*q.u to each row's scores: O unchanged,
     L shifted by scale*q.u (checked on the GPU outputs themselves)."""
