@@ -11,8 +11,8 @@
 // (key > query -> -inf), as in the Python reference.
 //
 // gfx950 mapping (not the pages' design):
-//  * One workgroup = 4 waves = 128 query rows of one (batch, head), one wave
-//    per SIMD; two workgroups share a CU. Key/value tiles of 64 rows stream
+//  * One workgroup = 8 waves = 256 query rows of one (batch, head), two
+//    waves per SIMD; each staged K/V tile serves 256 rows. Key/value tiles of 64 rows stream
 //    HBM -> VGPRs -> LDS through bounded buffer loads, written to LDS half an
 //    iteration after they are issued (K in the first half, V in the second);
 //    rings of 3 K and 2 V tiles, one s_barrier per iteration.
@@ -81,8 +81,8 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 
 }  // namespace
 
-// Waves per workgroup: one per SIMD.
-constexpr int kBf16Waves = 4;
+// Waves per workgroup: two per SIMD.
+constexpr int kBf16Waves = 8;
 
 template <int D, int WAVES>
 struct Bf16Cfg {
@@ -115,7 +115,7 @@ struct Bf16Cfg {
 };
 
 template <int D, int WAVES, bool CAUSAL, bool POS_SCALE>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int M, int N, int tiles_m, int n_wg, float c) {
