@@ -88,4 +88,26 @@ __device__ __forceinline__ int xcd_contiguous_id(int wg, int count) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
+// (head, query tile) of a workgroup. Each XCD gets whole heads (their query
+// tiles share K/V in its L2). Non-causal: the tiles of one head are
+// consecutive. Causal, when the heads split evenly over the XCDs: each XCD
+// runs the longest query tiles of all its heads first, then the next
+// longest, so the short tiles fill the tail; otherwise heads in order, each
+// longest tile first. Bijective onto heads x tiles for any count.
+struct TileId {
+  int bh, tm;
+};
+__device__ __forceinline__ TileId tile_order(int wg, int tiles_m, int heads, bool causal) {
+  const int count = tiles_m * heads;
+  if (causal && (heads & 7) == 0) {
+    const int hpx = heads >> 3;  // heads per XCD
+    const int xcd = wg & 7, idx = wg >> 3;
+    return {xcd * hpx + idx % hpx, tiles_m - 1 - idx / hpx};
+  }
+  const int wl = xcd_contiguous_id(wg, count);
+  const int bh = wl / tiles_m;
+  const int tm = wl - bh * tiles_m;
+  return {bh, causal ? tiles_m - 1 - tm : tm};
+}
+
 }  // namespace mi355

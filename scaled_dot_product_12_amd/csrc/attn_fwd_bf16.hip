@@ -118,7 +118,7 @@ template <int D, int WAVES, bool CAUSAL, bool POS_SCALE>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int M, int N, int tiles_m, int n_wg, float c) {
+    float* __restrict__ lse, int M, int N, int tiles_m, int heads, float c) {
   using C = Bf16Cfg<D, WAVES>;
   constexpr int NT = C::NT, BM = C::BM, BN = C::BN, ROWB = C::ROWB,
                 TILEB = C::TILEB, CPT = C::CPT, QSTEPS = C::QSTEPS, DBLK = C::DBLK,
@@ -132,10 +132,8 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_bf16_kernel(
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  const int wl = xcd_contiguous_id(workgroup_id(), n_wg);
-  const int bh = wl / tiles_m;
-  int tm = wl - bh * tiles_m;
-  if (CAUSAL) tm = tiles_m - 1 - tm;  // longest rows first
+  const TileId tile = tile_order(workgroup_id(), tiles_m, heads, CAUSAL);
+  const int bh = tile.bh, tm = tile.tm;
 
   const size_t q_off = (size_t)bh * M * D;
   const size_t kv_off = (size_t)bh * N * D;
@@ -543,7 +541,7 @@ static hipError_t launch_bf16_d(const LaunchArgs& a) {
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, WAVES, CAUSAL, POS>), grid,
                      dim3(WAVES * 64), 0, a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                     a.lse, (int)a.M, (int)a.N, tiles_m, tiles_m * (int)a.BH, a.scale * kLog2e);
+                     a.lse, (int)a.M, (int)a.N, tiles_m, (int)a.BH, a.scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ template <int D, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
-    int M, int N, int tiles_m, int n_wg, float c) {
+    int M, int N, int tiles_m, int heads, float c) {
   constexpr int NT = WAVES * 64;
   constexpr int BM = WAVES * 32;
   constexpr int BN = 32;
@@ -46,10 +46,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  const int wl = xcd_contiguous_id(workgroup_id(), n_wg);
-  const int bh = wl / tiles_m;
-  int tm = wl - bh * tiles_m;
-  if (CAUSAL) tm = tiles_m - 1 - tm;
+  const TileId tile = tile_order(workgroup_id(), tiles_m, heads, CAUSAL);
+  const int bh = tile.bh, tm = tile.tm;
 
   const size_t q_off = (size_t)bh * M * D;
   const size_t kv_off = (size_t)bh * N * D;
@@ -221,7 +219,7 @@ static hipError_t launch_f32_d(const LaunchArgs& a) {
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, WAVES, CAUSAL>), grid,
                      dim3(WAVES * 64), 0, a.stream, (const float*)a.q,
                      (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                     (int)a.M, (int)a.N, tiles_m, tiles_m * (int)a.BH, a.scale * kLog2e);
+                     (int)a.M, (int)a.N, tiles_m, (int)a.BH, a.scale * kLog2e);
   return hipGetLastError();
 }
 
