@@ -12,7 +12,8 @@
 // exact operand layout of the fp32 MFMA, and both products run on the matrix
 // cores (fp32 in, fp32 accumulate -- no precision is given up on fp32 inputs).
 //
-// One workgroup per (batch, head); one wave per block of 16 query rows.
+// One wave per block of 16 query rows; a workgroup holds up to four waves:
+// one head of up to 64 rows, or two (four) heads of up to 32 (16) rows.
 // With v_mfma_f32_16x16x4_f32, lane l = 16 g + n (n = l % 16, g = l / 16):
 //   S^T block kb (keys 16 kb .. 16 kb + 15 by queries q0 .. q0 + 15)
 //     A = K rows,   lane supplies K[16 kb + n][d],  d = g * D/4 + t
@@ -98,15 +99,17 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(kSmallQRows * 4 * 4) void attn_fwd_small_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv,
     const void* __restrict__ vv, void* __restrict__ ov, float* __restrict__ lse,
-    int M, int N, int causal, float c) {
+    int M, int N, int causal, float c, int BH, int waves_per_head) {
   constexpr int DQ = D / 4;    // contraction elements per lane group in QK^T
   constexpr int DB = D / 16;   // 16-wide d blocks of O
   const int tid = workitem_id();
   const int lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
-  const int q0 = (tid >> 6) * kSmallQRows;
+  const int wave = tid >> 6;
+  const int q0 = (wave % waves_per_head) * kSmallQRows;
   const int qi = q0 + n;
-  const size_t bh = workgroup_id();
+  const size_t bh = (size_t)workgroup_id() * (4 / waves_per_head) + wave / waves_per_head;
+  if (bh >= (size_t)BH) return;  // (no barrier in this kernel)
   const size_t q_off = bh * (size_t)M * D;
   const size_t kv_off = bh * (size_t)N * D;
   // Key blocks this wave needs: all of them, or under the causal mask only
@@ -201,13 +204,17 @@ hipError_t launch_small(const LaunchArgs& a, bool bf16) {
   if (a.M < 1 || a.M > kSmallMaxM || a.N < 1 || a.N > kSmallMaxN ||
       (a.D != 16 && a.D != 32))
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)a.BH);
-  const dim3 block((unsigned)(64 * ((a.M + kSmallQRows - 1) / kSmallQRows)));
+  // Short heads share a workgroup of up to four waves: fewer, larger
+  // workgroups launch faster.
+  const int wph = (int)((a.M + kSmallQRows - 1) / kSmallQRows);  // waves per head, 1..4
+  const int hpw = 4 / wph;                                         // heads per workgroup
+  const dim3 grid((unsigned)((a.BH + hpw - 1) / hpw));
+  const dim3 block((unsigned)(64 * wph * hpw));
   const float c = a.scale * kLog2e;
   const int M = (int)a.M, N = (int)a.N, causal = (int)a.causal;
 #define MI355_SMALL_LAUNCH(BF, DD)                                                   \
   hipLaunchKernelGGL((attn_fwd_small_kernel<BF, DD>), grid, block, 0, a.stream, a.q, \
-                     a.k, a.v, a.o, a.lse, M, N, causal, c)
+                     a.k, a.v, a.o, a.lse, M, N, causal, c, (int)a.BH, wph)
   if (bf16) {
     if (a.D == 16) MI355_SMALL_LAUNCH(true, 16);
     else MI355_SMALL_LAUNCH(true, 32);
