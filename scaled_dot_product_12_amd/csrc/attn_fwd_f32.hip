@@ -14,19 +14,34 @@
 //  * Key tiles are 32 wide. The second product contracts over two keys per
 //    MFMA (one per lane half), so its A operand (V^T) is one fp32 from a
 //    row-major V tile and V needs no transpose.
+//  * Small problems split each row block's keys over 2 or 4 waves of the
+//    workgroup and merge the partial (O, m, l) through LDS, so that all
+//    SIMDs get an even share (the merge is the one-step combination used to
+//    join key-split partial softmaxes: rescale each part to the common max
+//    and add).
 
 #include "attn_device.h"
 #include "attn_launch.h"
 
 namespace mi355 {
 
-template <int D, int WAVES, bool CAUSAL>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
+// Waves per workgroup. Wave w takes query rows 32*(w % R) .. +31 of the
+// workgroup's tile and key part w / R (KS parts, R = 4 / KS row blocks):
+// part p works on key tiles j with j % KS == p, and the KS partial
+// results of a row block are merged through LDS at the end. KS > 1 is for
+// problems with few 32-row blocks, where one block per wave would leave
+// SIMDs idle or unevenly loaded.
+constexpr int kF32Waves = 4;
+
+template <int D, int KS, bool CAUSAL>
+__global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
     int M, int N, int tiles_m, int heads, float c) {
+  constexpr int WAVES = kF32Waves;
   constexpr int NT = WAVES * 64;
-  constexpr int BM = WAVES * 32;
+  constexpr int R = WAVES / KS;        // 32-row blocks per workgroup
+  constexpr int BM = R * 32;
   constexpr int BN = 32;
   constexpr int HALF = D / 2;          // d values per lane half
   constexpr int KSTR = D + 4;          // floats per K row in LDS
@@ -35,16 +50,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
   constexpr int DBLK = DP / 32;
   constexpr int DCH = D / 4;           // 16-byte chunks per row
   constexpr int CH = BN * DCH;         // chunks per K (or V) tile
-  constexpr int CPT = (CH + NT - 1) / NT;
+  constexpr int CPT = (KS * CH + NT - 1) / NT;  // chunks per thread per step (KS tiles)
+  constexpr int TILE_F = BN * KSTR + BN * VSTR;  // floats per staged K+V tile
+  // partial results of parts 1.. : per lane DBLK*16 accumulators, m, l
+  constexpr int PART_F = 64 * (DBLK * 16 + 2);
+  constexpr int MERGE_F = (KS - 1) * R * PART_F;
+  constexpr int SMEM_F = KS * TILE_F > MERGE_F ? KS * TILE_F : MERGE_F;
 
-  __shared__ __attribute__((aligned(16))) float Ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) float Vs[BN * VSTR];
+  __shared__ __attribute__((aligned(16))) float smem[SMEM_F];
 
   const int tid = workitem_id();
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int rb = wave % R, part = wave / R;
   const int r32 = lane & 31;
   const int g = lane >> 5;
+  float* Ks = smem + part * TILE_F;
+  float* Vs = Ks + BN * KSTR;
 
   const TileId tile = tile_order(workgroup_id(), tiles_m, heads, CAUSAL);
   const int bh = tile.bh, tm = tile.tm;
@@ -56,7 +78,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
   const float* vh = v + kv_off;
 
   const int q_wg0 = tm * BM;
-  const int qw0 = q_wg0 + wave * 32;
+  const int qw0 = q_wg0 + rb * 32;
   const int qi = qw0 + r32;
   const bool wave_live = qw0 < M;
   const int wave_last = min(qw0 + 31, M - 1);
@@ -76,26 +98,29 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
     const int q_last = min(q_wg0 + BM, M) - 1;
     nt = min(nt, q_last / BN + 1);
   }
+  const int steps = (nt + KS - 1) / KS;
 
   if (D < 32) {  // V columns D..31 stay zero
-    for (int idx = tid; idx < BN * (DP - D); idx += NT) {
-      const int row = idx / (DP - D);
-      Vs[row * VSTR + D + (idx - row * (DP - D))] = 0.0f;
+    for (int idx = tid; idx < KS * BN * (DP - D); idx += NT) {
+      const int pp = idx / (BN * (DP - D)), rem = idx - pp * (BN * (DP - D));
+      const int row = rem / (DP - D);
+      smem[pp * TILE_F + BN * KSTR + row * VSTR + D + (rem - row * (DP - D))] = 0.0f;
     }
   }
 
+  // Step s stages tile s*KS + pp into buffer pp, for every part pp.
   f32x4_t kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int j) {
-    const int key0 = j * BN;
+  auto load_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int ch = tid + u * NT;
-      if (ch < CH) {
-        const int row = ch / DCH;
-        const int col = (ch - row * DCH) * 4;
-        const int key = key0 + row;
+      if (ch < KS * CH) {
+        const int pp = ch / CH, cl = ch - pp * CH;
+        const int row = cl / DCH;
+        const int col = (cl - row * DCH) * 4;
+        const int key = (st * KS + pp) * BN + row;
         f32x4_t xk = {0.0f, 0.0f, 0.0f, 0.0f}, xv = xk;
-        if (key < N) {
+        if (key < min(N, nt * BN)) {
           xk = *(const f32x4_t*)(kh + (size_t)key * D + col);
           xv = *(const f32x4_t*)(vh + (size_t)key * D + col);
         }
@@ -104,17 +129,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_step = [&]() {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int ch = tid + u * NT;
-      if (ch < CH) {
-        const int row = ch / DCH;
-        const int col = (ch - row * DCH) * 4;
-        *(f32x4_t*)(Ks + row * KSTR + col) = kreg[u];
+      if (ch < KS * CH) {
+        const int pp = ch / CH, cl = ch - pp * CH;
+        const int row = cl / DCH;
+        const int col = (cl - row * DCH) * 4;
+        float* kb = smem + pp * TILE_F;
+        float* vb = kb + BN * KSTR;
+        *(f32x4_t*)(kb + row * KSTR + col) = kreg[u];
         f32x2_t lo = {vreg[u][0], vreg[u][1]}, hi = {vreg[u][2], vreg[u][3]};
-        *(f32x2_t*)(Vs + row * VSTR + col) = lo;
-        *(f32x2_t*)(Vs + row * VSTR + col + 2) = hi;
+        *(f32x2_t*)(vb + row * VSTR + col) = lo;
+        *(f32x2_t*)(vb + row * VSTR + col + 2) = hi;
       }
     }
   };
@@ -129,14 +157,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
 
-  if (nt > 0) load_tile(0);
-  for (int j = 0; j < nt; ++j) {
+  if (steps > 0) load_step(0);
+  for (int st = 0; st < steps; ++st) {
     __syncthreads();
-    store_tile();
+    store_step();
     __syncthreads();
-    if (j + 1 < nt) load_tile(j + 1);
+    if (st + 1 < steps) load_step(st + 1);
+    const int j = st * KS + part;
     const int key0 = j * BN;
-    if (!wave_live) continue;
+    if (!wave_live || j >= nt) continue;
     if (CAUSAL && key0 > wave_last) continue;
 
     // S^T = K (cQ)^T, one 32-key block: lane owns keys g*16 + i.
@@ -191,6 +220,39 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
     }
   }
 
+  // Merge the key parts of each row block (same lane layout in every part):
+  // m = max_p m_p, O = sum_p 2^(m_p - m) O_p, l = sum_p 2^(m_p - m) l_p.
+  if (KS > 1) {
+    __syncthreads();  // every wave is done with the staged tiles
+    if (part > 0) {
+      float* dstp = smem + ((part - 1) * R + rb) * PART_F + lane;
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dstp[(b * 16 + i) * 64] = acc[b][i];
+      dstp[(DBLK * 16) * 64] = m_run;
+      dstp[(DBLK * 16 + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (part > 0) return;
+#pragma unroll
+    for (int pp = 1; pp < KS; ++pp) {
+      const float* srcp = smem + ((pp - 1) * R + rb) * PART_F + lane;
+      const float m_p = srcp[(DBLK * 16) * 64];
+      const float l_p = srcp[(DBLK * 16 + 1) * 64];
+      const float m_new = fmaxf(m_run, m_p);
+      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+      const float a_self = __builtin_amdgcn_exp2f(m_run - m_ref);
+      const float a_p = __builtin_amdgcn_exp2f(m_p - m_ref);
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] = acc[b][i] * a_self + srcp[(b * 16 + i) * 64] * a_p;
+      l_run = l_run * a_self + l_p * a_p;
+      m_run = m_new;
+    }
+  }
+
   if (!wave_live) return;
   const float l_tot = half_pair_sum(l_run);
   if (qi >= M) return;
@@ -210,17 +272,32 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(
   if (g == 0) lse[(size_t)bh * M + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
-template <int D, bool CAUSAL>
-static hipError_t launch_f32_d(const LaunchArgs& a) {
-  constexpr int WAVES = 4;
-  constexpr int BM = WAVES * 32;
+// Key parts per row block: 1 when the problem has at least two 32-row blocks
+// per SIMD (1024 SIMDs), else split the keys so that every SIMD gets work.
+static int f32_key_split(int64_t BH, int64_t M) {
+  const int64_t blocks = BH * ((M + 31) / 32);
+  return blocks >= 2048 ? 1 : (blocks >= 512 ? 2 : 4);
+}
+
+template <int D, int KS, bool CAUSAL>
+static hipError_t launch_f32_dk(const LaunchArgs& a) {
+  constexpr int BM = (kF32Waves / KS) * 32;
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const dim3 grid((unsigned)(tiles_m * a.BH));
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, WAVES, CAUSAL>), grid,
-                     dim3(WAVES * 64), 0, a.stream, (const float*)a.q,
-                     (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                     (int)a.M, (int)a.N, tiles_m, (int)a.BH, a.scale * kLog2e);
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, KS, CAUSAL>), grid, dim3(kF32Waves * 64), 0,
+                     a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                     (float*)a.o, a.lse, (int)a.M, (int)a.N, tiles_m, (int)a.BH,
+                     a.scale * kLog2e);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_f32_d(const LaunchArgs& a) {
+  switch (f32_key_split(a.BH, a.M)) {
+    case 1: return launch_f32_dk<D, 1, CAUSAL>(a);
+    case 2: return launch_f32_dk<D, 2, CAUSAL>(a);
+    default: return launch_f32_dk<D, 4, CAUSAL>(a);
+  }
 }
 
 template <int D>
@@ -238,6 +315,7 @@ hipError_t launch_main_f32(const LaunchArgs& a) {
   }
 }
 
-int main_f32_tile_rows() { return 4 * 32; }
+// Smallest query tile of any launch (KS = 4): the grid-size check uses it.
+int main_f32_tile_rows() { return 32; }
 
 }  // namespace mi355

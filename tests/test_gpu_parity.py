@@ -44,6 +44,14 @@ def test_main_kernel_shapes(dtype, D, causal):
                    label=f"shape{i}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_unsplit_launch(causal):
+    """fp32 with at least 2048 blocks of 32 query rows: one wave per row
+    block and key range (the launch the smaller fp32 shapes do not use)."""
+    q, k, v = make_qkv(4, 16, 1024, 200, 64, "fp32", seed=48)
+    check_full(q, k, v, causal, f32(0.125), path=MAIN, label="fp32-unsplit")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("D", [16, 32])
 @pytest.mark.parametrize("causal", [False, True])
