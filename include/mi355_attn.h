@@ -55,7 +55,7 @@ extern "C" {
 /* Kernel paths (attn_fwd_path / attn_fwd_select_path). */
 #define MI355_ATTN_PATH_AUTO  0 /* let the library choose                        */
 #define MI355_ATTN_PATH_MAIN  1 /* tiled MFMA kernel with the online softmax      */
-#define MI355_ATTN_PATH_SMALL 2 /* one-tile, LDS-resident kernel for short rows   */
+#define MI355_ATTN_PATH_SMALL 2 /* one-tile, register-resident short-row kernel */
 
 /*
  * attn_fwd -- O and L of scaled-dot-product attention (see the top of this
@@ -113,8 +113,9 @@ int attn_fwd_path(const void *q, const void *k, const void *v, void *o,
 /*
  * attn_fwd_select_path -- which kernel PATH_AUTO runs for this problem
  * (MI355_ATTN_PATH_MAIN or MI355_ATTN_PATH_SMALL), or -1 if the sizes are
- * invalid or unsupported. The small kernel holds one whole sequence per
- * workgroup: it is chosen for M <= 64, N <= 64 and D <= 32. Pure host logic.
+ * invalid or unsupported. The small kernel keeps a whole (batch, head)
+ * sequence in the registers of one to four waves (one per 16 query rows):
+ * it is chosen for M <= 64, N <= 64 and D <= 32. Pure host logic.
  */
 int attn_fwd_select_path(int64_t B, int64_t H, int64_t M, int64_t N,
                          int64_t D, int is_causal, int dtype);
