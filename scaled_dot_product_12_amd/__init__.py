@@ -138,6 +138,8 @@ def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
         if (tuple(lse.shape) != (B, H, M) or lse.dtype != torch.float32
                 or not lse.is_contiguous()):
             raise ValueError("out[1] must be a contiguous fp32 [B, H, M] tensor")
+        if o.device != q.device or lse.device != q.device:
+            raise ValueError("out tensors must be on q's device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = lib().attn_fwd_path(q.data_ptr(), k.data_ptr(), v.data_ptr(),

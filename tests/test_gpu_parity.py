@@ -201,6 +201,15 @@ def test_empty_problem_launches_nothing():
     assert o.shape == (1, 2, 0, 64)
 
 
+def test_out_tensors_must_be_on_the_device():
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 1, 8, 16, device=dev)
+    with pytest.raises(ValueError, match="device"):
+        attn.attn_fwd(q, q, q, out=(torch.empty(1, 1, 8, 16), torch.empty(1, 1, 8)))
+    with pytest.raises(ValueError, match="device"):
+        attn.attn_fwd(q, q, q, out=(torch.empty_like(q), torch.empty(1, 1, 8)))
+
+
 def test_small_path_rejects_large_shapes():
     dev = torch.device("cuda:0")
     q = torch.zeros(1, 1, 65, 16, device=dev)
