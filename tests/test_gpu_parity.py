@@ -201,6 +201,22 @@ def test_empty_problem_launches_nothing():
     assert o.shape == (1, 2, 0, 64)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_random_problem_sweep(dtype):
+    """Seeded random problems (sizes 1..300, every supported D, causal or
+    not, scales of either sign), each compared element by element with the
+    oracle: tails, masks and the choice of kernel in many combinations."""
+    rng = np.random.default_rng(4242 if dtype == "bf16" else 4243)
+    for case in range(24):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        M, N = int(rng.integers(1, 301)), int(rng.integers(1, 301))
+        D = int(rng.choice([16, 32, 64, 128]))
+        causal = bool(rng.integers(0, 2))
+        scale = f32(rng.uniform(-1.0, 1.0) * 2.0 / math.sqrt(D))
+        q, k, v = make_qkv(B, H, M, N, D, dtype, seed=5000 + case)
+        check_full(q, k, v, causal, scale, label=f"sweep{case}", magnitude_tol=True)
+
+
 def test_out_tensors_must_be_on_the_device():
     dev = torch.device("cuda:0")
     q = torch.zeros(1, 1, 8, 16, device=dev)
