@@ -18,10 +18,18 @@ one value per query row, [B, H, M]).
 Inputs are widened to fp64 exactly (fp32 and bf16 values are representable),
 so for bf16 the oracle sees the bf16-rounded values the GPU sees.
 
-Parity pins (tests/test_oracle_pins.py): a 50-digit ``decimal`` brute force,
-an independent fp64 re-implementation of the pages' tiled online algorithm,
-torch's fp64 CPU SDPA, and closed forms / invariants. Every function here is
-pinned.
+The gradient (``attn_bwd``, ``attn_bwd_heads``; see ``attn_oracle_bwd.c``) is
+the chain rule through softmax attention, dQ, dK, dV for an upstream dO, with
+the softmax Jacobian written out; "Blackwell Attention Example" (backward
+kernel and autograd function sections) evaluates the same quantity tile by
+tile.
+
+Parity pins (tests/test_oracle_pins.py, tests/test_oracle_bwd_pins.py): a
+50-digit ``decimal`` brute force, an independent fp64 re-implementation of the
+pages' tiled online algorithm, torch's fp64 CPU SDPA, and closed forms /
+invariants for the forward; central finite differences of the forward,
+torch's fp64 autograd, an fp64 restatement of the pages' tiled backward, and
+closed forms / invariants for the gradient. Every function here is pinned.
 """
 from __future__ import annotations
 
@@ -55,6 +63,10 @@ def _load():
                                          ctypes.POINTER(ctypes.c_int64), i64,
                                          ctypes.c_int]
         lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64,
+                                        i64, i64, ctypes.c_double, ctypes.c_int,
+                                        ctypes.c_int]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -147,3 +159,45 @@ def attn_rows(q, k, v, rows: Iterable[Tuple[int, int, int]],
             out_o[t] = o[n]
             out_l[t] = lse[n]
     return out_o, out_l
+
+
+def attn_bwd(q, k, v, dout, is_causal: bool = False, scale: float | None = None,
+             nthreads: int | None = None):
+    """Gradient of attention for upstream ``dout`` [B,H,M,D]: returns
+    (dQ [B,H,M,D], dK [B,H,N,D], dV [B,H,N,D]) as fp64 numpy arrays."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, M, N, D = _shapes(q, k, v)
+    if g.shape != q.shape:
+        raise ValueError(f"dout {g.shape} must have q's shape {q.shape}")
+    if M > 0 and N < 1:
+        raise ValueError("no keys")
+    if scale is None:
+        scale = default_scale(D)
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), B, H, M, N, D, float(scale),
+                                 int(bool(is_causal)), nthreads or host_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd failed with {rc}")
+    return dq, dk, dv
+
+
+def attn_bwd_heads(q, k, v, dout, heads: Iterable[Tuple[int, int]],
+                   is_causal: bool = False, scale: float | None = None,
+                   nthreads: int | None = None):
+    """Gradient for selected heads (b, h) only: returns lists of per-head
+    (dQ [M,D], dK [N,D], dV [N,D]) in fp64, in the order given. Only those
+    heads are widened, so this stays usable on inputs far larger than the
+    full oracle could finish."""
+    out = []
+    for b, h in heads:
+        b, h = int(b), int(h)
+        if not (0 <= b < q.shape[0] and 0 <= h < q.shape[1]):
+            raise ValueError(f"head {(b, h)} out of range")
+        one = [x[b:b + 1, h:h + 1] for x in (q, k, v, dout)]
+        dq, dk, dv = attn_bwd(*one, is_causal=is_causal, scale=scale,
+                              nthreads=nthreads)
+        out.append((dq[0, 0], dk[0, 0], dv[0, 0]))
+    return out

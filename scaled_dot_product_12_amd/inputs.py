@@ -6,7 +6,10 @@ them. Both the HIP path's tests/benchmark and the CPU oracle are fed from here.
 Recipe (every workload): ``g = torch.Generator("cpu").manual_seed(seed)``, then
 Q, K, V in that order, each ``torch.randn(shape, dtype=float32, generator=g)``.
 bf16 workloads round those fp32 draws to bf16 with ``.to(torch.bfloat16)``
-(round-to-nearest-even). Shapes follow the pages' workloads:
+(round-to-nearest-even). The upstream gradient dO of a backward problem is
+drawn the same way from its own generator, seeded with ``seed + DOUT_SEED_OFFSET``
+(so Q, K, V are the same draws as the forward problem's). Shapes follow the
+pages' workloads:
 
 * "Extend Thunder with CUDA-Python": Q, K, V of shape (96, 512, 128), fp32.
 * "Blackwell Attention Example", test harness: bf16 (z, h, n_ctx, head_dim)
@@ -95,6 +98,17 @@ def make_qkv(B: int, H: int, M: int, N: int, D: int, dtype: str = "fp32",
     if dtype != "fp32":
         q, k, v = (t.to(_DT[dtype]) for t in (q, k, v))
     return q, k, v
+
+
+DOUT_SEED_OFFSET = 7919
+
+
+def make_dout(B: int, H: int, M: int, D: int, dtype: str = "fp32",
+              seed: int = 0) -> torch.Tensor:
+    """Upstream gradient dO [B,H,M,D] on the CPU, contiguous."""
+    g = torch.Generator("cpu").manual_seed(seed + DOUT_SEED_OFFSET)
+    t = torch.randn((B, H, M, D), dtype=torch.float32, generator=g)
+    return t if dtype == "fp32" else t.to(_DT[dtype])
 
 
 # Axial images: 4 images of 32 x 32 tokens, 4 heads of dim 16.
