@@ -120,6 +120,65 @@ int attn_fwd_path(const void *q, const void *k, const void *v, void *o,
 int attn_fwd_select_path(int64_t B, int64_t H, int64_t M, int64_t N,
                          int64_t D, int is_causal, int dtype);
 
+/*
+ * attn_bwd -- gradient of attention with respect to q, k and v (the backward
+ * of "Blackwell Attention Example": preprocess kernel, backward kernel and
+ * autograd function sections). For the forward above and an upstream
+ * gradient dO, with P_ij = exp(s_ij - L_i) (zero where masked):
+ *
+ *     delta_i = sum_d O[i,d] * dO[i,d]
+ *     dV_j    = sum_i P_ij dO_i
+ *     dS_ij   = P_ij (<dO_i, v_j> - delta_i)
+ *     dQ_i    = scale * sum_j dS_ij k_j
+ *     dK_j    = scale * sum_i dS_ij q_i
+ *
+ *   q, k, v    the forward's inputs (device, element type `dtype`).
+ *   o, lse     the forward's outputs for the same q, k, v, scale and
+ *              is_causal (attn_fwd's O and natural-log L).
+ *   dout       upstream gradient dO, [B,H,M,D], element type `dtype`.
+ *   dq         output [B,H,M,D]; dk, dv outputs [B,H,N,D]; element type
+ *              `dtype`. Every element is written (dk, dv rows that no query
+ *              sees get zeros).
+ *   delta      caller-owned device workspace of B*H*M fp32 values; after the
+ *              call's work completes it holds delta_i. Its prior contents are
+ *              ignored.
+ *   B, H, M, N, D, scale, is_causal, dtype, stream  as for attn_fwd, except
+ *              that N may be 0 when M is 0.
+ *
+ * Enqueues two kernels on `stream` (dQ and delta first, then dK and dV) and
+ * returns without synchronising; results are deterministic (no atomics).
+ *
+ * Returns MI355_ATTN_OK, or:
+ *   INVALID_ARG  a null k, v, dk or dv while B*H*N > 0, or any null pointer
+ *                while B*H*M > 0 (with M == 0 the query-side pointers are
+ *                not used); B, H, M, N < 0; N < 1
+ *                while B*H*M > 0; D < 1; non-finite scale; is_causal not 0/1;
+ *                bad dtype; dq, dk, dv or delta overlapping an input or each
+ *                other (inputs may alias).
+ *   UNSUPPORTED  dtype MI355_ATTN_FP32; D not in {32, 64, 128}; a size whose
+ *                element count or launch grid does not fit the kernels'
+ *                index types.
+ *   MISALIGNED   q, k, v, o, dout, dq, dk or dv not 16-byte aligned, or lse
+ *                or delta not 4-byte aligned.
+ *   HIP_ERROR    a launch failed (hipGetLastError).
+ * B*H*(M+N) == 0 returns OK without launching.
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o,
+             const float *lse, const void *dout, void *dq, void *dk, void *dv,
+             float *delta, int64_t B, int64_t H, int64_t M, int64_t N,
+             int64_t D, float scale, int is_causal, int dtype, void *stream);
+
+/*
+ * attn_bwd_validate -- the status attn_bwd would return for these arguments
+ * before launching (never HIP_ERROR). No HIP call, no dereference.
+ */
+int attn_bwd_validate(const void *q, const void *k, const void *v,
+                      const void *o, const float *lse, const void *dout,
+                      const void *dq, const void *dk, const void *dv,
+                      const float *delta, int64_t B, int64_t H, int64_t M,
+                      int64_t N, int64_t D, float scale, int is_causal,
+                      int dtype);
+
 /* attn_status_string -- a static, NUL-terminated name for a status code
  * ("unknown status" for values outside the list above). */
 const char *attn_status_string(int status);

@@ -7,7 +7,9 @@ torch tensors, allocates O and L, and calls the C ``attn_fwd`` on torch's
 current stream -- the interface of the pages' wrappers
 (``flash_attention_reference(Q, K, V, is_causal=False, scale=None) -> (O, L)``
 in "Extend Thunder with CUDA-Python"; ``(q, k, v) -> (o, lse)`` in
-"Blackwell Attention Example").
+"Blackwell Attention Example"). ``attn_bwd`` takes the forward's inputs and
+outputs and the upstream gradient dO and returns (dQ, dK, dV), as the
+backward of that page's autograd function does.
 
 There is no fallback: if the HIP library is missing, every call raises.
 """
@@ -34,7 +36,8 @@ MI355_ATTN_PATH_MAIN = 1
 MI355_ATTN_PATH_SMALL = 2
 
 EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
-           "attn_fwd_select_path", "attn_status_string")
+           "attn_fwd_select_path", "attn_status_string", "attn_bwd",
+           "attn_bwd_validate")
 
 _lib = None
 
@@ -60,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_validate.restype = cint
         L.attn_fwd_select_path.argtypes = [i64, i64, i64, i64, i64, cint, cint]
         L.attn_fwd_select_path.restype = cint
+        L.attn_bwd.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint, vp]
+        L.attn_bwd.restype = cint
+        L.attn_bwd_validate.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint]
+        L.attn_bwd_validate.restype = cint
         L.attn_status_string.argtypes = [cint]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -74,6 +81,13 @@ def attn_fwd_validate(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype) -
     """Status attn_fwd would return; pointers are ints (addresses) or None."""
     return lib().attn_fwd_validate(q, k, v, o, lse, B, H, M, N, D, float(scale),
                                    int(is_causal), int(dtype))
+
+
+def attn_bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D, scale,
+                      is_causal, dtype) -> int:
+    """Status attn_bwd would return; pointers are ints (addresses) or None."""
+    return lib().attn_bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N,
+                                   D, float(scale), int(is_causal), int(dtype))
 
 
 def attn_fwd_select_path(B, H, M, N, D, is_causal, dtype) -> int:
@@ -149,3 +163,51 @@ def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
     if st != MI355_ATTN_OK:
         raise RuntimeError(f"attn_fwd failed: {attn_status_string(st)} ({st})")
     return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
+             scale: Optional[float] = None, out: Optional[Tuple] = None,
+             delta=None):
+    """(dQ, dK, dV) of attention for the upstream gradient ``dout``.
+
+    ``q, k, v`` are the forward's inputs, ``o, lse`` its outputs (from
+    ``attn_fwd`` with the same ``is_causal`` and ``scale``), ``dout`` has o's
+    shape and dtype. Gradients have the inputs' dtype. ``out=(dq, dk, dv)``
+    writes into preallocated tensors; ``delta`` is an optional fp32 [B, H, M]
+    workspace (allocated here if None) that receives rowsum(O * dO). bf16
+    only, D in {32, 64, 128}. Asynchronous on torch's current stream.
+    """
+    import torch
+    B, H, M, N, D = _check(q, k, v)
+    dt = _dtype_code(q)
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
+        if (t.shape != shape or t.dtype != q.dtype or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if (tuple(lse.shape) != (B, H, M) or lse.dtype != torch.float32
+            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 [B, H, M] tensor on q's device")
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            if (t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous()
+                    or t.device != q.device):
+                raise ValueError(f"out {name} must be a contiguous tensor like {name[1]}")
+    if delta is None:
+        delta = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    elif (tuple(delta.shape) != (B, H, M) or delta.dtype != torch.float32
+          or not delta.is_contiguous() or delta.device != q.device):
+        raise ValueError("delta must be a contiguous fp32 [B, H, M] tensor on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), delta.data_ptr(), B, H, M, N, D, float(scale),
+                            int(bool(is_causal)), dt, stream)
+    if st != MI355_ATTN_OK:
+        raise RuntimeError(f"attn_bwd failed: {attn_status_string(st)} ({st})")
+    return dq, dk, dv

@@ -71,6 +71,62 @@ int validate(const void* q, const void* k, const void* v, const void* o,
   return MI355_ATTN_OK;
 }
 
+bool bwd_supported_d(int64_t D) { return D == 32 || D == 64 || D == 128; }
+
+int validate_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, const void* dq, const void* dk,
+                 const void* dv, const float* delta, int64_t B, int64_t H, int64_t M,
+                 int64_t N, int64_t D, float scale, int is_causal, int dtype) {
+  if (B < 0 || H < 0 || M < 0 || N < 0 || D < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (dtype != MI355_ATTN_FP32 && dtype != MI355_ATTN_BF16) return MI355_ATTN_ERR_INVALID_ARG;
+  if (is_causal != 0 && is_causal != 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MI355_ATTN_ERR_INVALID_ARG;
+  int64_t BH, q_rows, k_rows;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, M, &q_rows) || !mul_ok(BH, N, &k_rows))
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (q_rows == 0 && k_rows == 0) return MI355_ATTN_OK;  // nothing to compute
+  if (M > 0 && N < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  // Key-side buffers are always used here; with no query rows the query-side
+  // ones are never touched (dK = dV = 0) and may be null.
+  if (!k || !v || !dk || !dv) return MI355_ATTN_ERR_INVALID_ARG;
+  if (q_rows > 0 && (!q || !o || !lse || !dout || !dq || !delta))
+    return MI355_ATTN_ERR_INVALID_ARG;
+  if (dtype != MI355_ATTN_BF16 || !bwd_supported_d(D)) return MI355_ATTN_ERR_UNSUPPORTED;
+
+  const int64_t es = 2;
+  int64_t md, nd, q_elems, kv_elems, q_bytes, kv_bytes, row_bytes;
+  if (!mul_ok(M, D, &md) || !mul_ok(N, D, &nd) || md > kIntMax || nd > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (!mul_ok(q_rows, D, &q_elems) || !mul_ok(k_rows, D, &kv_elems) ||
+      !mul_ok(q_elems, es, &q_bytes) || !mul_ok(kv_elems, es, &kv_bytes) ||
+      !mul_ok(q_rows, 4, &row_bytes))
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  const int64_t tq = mi355::bwd_dq_tile_rows(), tk = mi355::bwd_dkdv_tile_rows();
+  int64_t grid_q, grid_k;
+  if (!mul_ok((M + tq - 1) / tq, BH, &grid_q) || grid_q > kIntMax ||
+      !mul_ok((N + tk - 1) / tk, BH, &grid_k) || grid_k > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return MI355_ATTN_ERR_MISALIGNED;
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3u) return MI355_ATTN_ERR_MISALIGNED;
+
+  // Outputs (dq, dk, dv, delta) must not overlap the inputs or each other
+  // (inputs may alias one another).
+  const void* in_p[6] = {q, k, v, o, lse, dout};
+  const int64_t in_n[6] = {q_bytes, kv_bytes, kv_bytes, q_bytes, row_bytes, q_bytes};
+  const void* out_p[4] = {dq, dk, dv, delta};
+  const int64_t out_n[4] = {q_bytes, kv_bytes, kv_bytes, row_bytes};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlap(out_p[a], out_n[a], in_p[b], in_n[b])) return MI355_ATTN_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(out_p[a], out_n[a], out_p[b], out_n[b])) return MI355_ATTN_ERR_INVALID_ARG;
+  }
+  return MI355_ATTN_OK;
+}
+
 int select_path(int64_t M, int64_t N, int64_t D) {
   return small_fits(M, N, D) ? MI355_ATTN_PATH_SMALL : MI355_ATTN_PATH_MAIN;
 }
@@ -136,6 +192,43 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int is_causal, int dtype, void* stream) {
   return attn_fwd_path(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype,
                        MI355_ATTN_PATH_AUTO, stream);
+}
+
+int attn_bwd_validate(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, const void* dq, const void* dk,
+                      const void* dv, const float* delta, int64_t B, int64_t H, int64_t M,
+                      int64_t N, int64_t D, float scale, int is_causal, int dtype) {
+  return validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D, scale,
+                      is_causal, dtype);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B,
+             int64_t H, int64_t M, int64_t N, int64_t D, float scale, int is_causal,
+             int dtype, void* stream) {
+  const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D,
+                              scale, is_causal, dtype);
+  if (st != MI355_ATTN_OK) return st;
+  if (B * H * (M + N) == 0) return MI355_ATTN_OK;
+  mi355::BwdLaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.BH = B * H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.causal = is_causal != 0;
+  a.stream = (hipStream_t)stream;
+  return mi355::launch_bwd_bf16(a) == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 
 const char* attn_status_string(int status) {

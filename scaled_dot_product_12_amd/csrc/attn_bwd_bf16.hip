@@ -1,0 +1,550 @@
+// attn_bwd_bf16.hip -- FlashAttention-2 backward for bf16 inputs on gfx950.
+//
+// The gradient of O = softmax(scale Q K^T [+ causal mask]) V for an upstream
+// dO, in the tiled form of "Blackwell Attention Example" (backward kernel
+// implementation section): the probabilities are recomputed tile by tile from
+// the saved logsumexp (P = exp2(scale log2(e) q.k - log2(e) L)), the row term
+// is delta_i = rowsum(O_i * dO_i) (its preprocess kernel), and
+//     dV += P^T dO,   dP = dO V^T,   dS = P (dP - delta),
+//     dK += dS^T Q (times scale),    dQ += dS K (times scale).
+// P and dS are rounded to bf16 before their products, which accumulate in
+// fp32, as on that page.
+//
+// gfx950 mapping (not the page's design, which accumulates dQ with atomics
+// from the key-tile loop): two kernels, so that every output element has one
+// writer and the result is run-to-run deterministic.
+//  * attn_bwd_dq_kernel: one workgroup = 8 waves = 256 query rows of one
+//    (batch, head); loops over key/value tiles of 64 rows. It first forms
+//    delta for its rows (O and dO rows in registers) and writes it out for the
+//    second kernel. Per tile: S^T = K Q^T and dP^T = V dO^T (K, V rows from
+//    LDS, Q^T, dO^T in registers), P^T and dS^T in registers, then
+//    dQ^T += K^T dS^T with K^T read from LDS through ds_read_b64_tr_b16.
+//  * attn_bwd_dkdv_kernel: one workgroup = 4 waves = 128 key rows; loops over
+//    query tiles of 64 rows. Per tile: S = Q K^T, dP = dO V^T (Q, dO rows from
+//    LDS, K^T, V^T in registers), P and dS, then dV^T += dO^T P and
+//    dK^T += Q^T dS with dO^T, Q^T read transposed from LDS.
+//  * All products are v_mfma_f32_32x32x16_bf16. Every staged tile is stored
+//    with its rows permuted so that the 16 accumulator registers of a lane
+//    are 16 consecutive rows of the tile: rounded to bf16 those registers are
+//    directly the B operand of the next product. Tiles are XOR-swizzled at
+//    16-byte granularity.
+//  * Tiles stream HBM -> VGPRs -> LDS through bounded buffer loads (rows past
+//    the head read as zeros), double-buffered, one barrier per tile.
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace mi355 {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4_t __attribute__((address_space(3)))*)(lds_u8*)p);
+}
+
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format, no swizzle): loads past num_records return zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+constexpr int kDqWaves = 8;    // dQ kernel: 256 query rows per workgroup
+constexpr int kDkvWaves = 4;   // dK/dV kernel: 128 key rows per workgroup
+constexpr int kTileRows = 64;  // rows of a staged K/V (or Q/dO) tile
+
+// A staged 64-row tile of a [rows, D] bf16 tensor in LDS.
+// LDS row R holds source row perm(R); within a row, 16-byte chunk position p
+// holds source chunk p ^ swz(R). perm is a bit permutation of the low five
+// row bits: after a 32x32 MFMA whose A operand reads rows blk*32 + (lane%32),
+// accumulator register r of lane l belongs to source row
+// blk*32 + 16*(l/32) + r.
+template <int D>
+struct Tile {
+  static constexpr int ROWB = 2 * D;                 // bytes per row
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int BYTES = kTileRows * ROWB;
+  static constexpr int CHUNKS = BYTES / 16;
+  static constexpr int QSTEPS = D / 16;              // 16-wide d steps
+  static constexpr int DBLK = D / 32;                // 32-wide d blocks
+  __device__ static constexpr int perm(int r) {
+    const int b = r & 31;
+    return (r & ~31) + ((b >> 2) & 1) * 16 + (b >> 3) * 4 + (b & 3);
+  }
+  __device__ static constexpr int swz(int r) { return (r & 15) & (CPR - 1); }
+};
+
+// Staging of one tile by NT threads: thread chunk u is LDS chunk
+// ch = tid + u*NT (row ch / CPR, position ch % CPR).
+template <int D, int NT>
+struct Stager {
+  using T = Tile<D>;
+  static constexpr int CPT = (T::CHUNKS + NT - 1) / NT;
+  int src[CPT];  // byte offset of the source chunk from the tile's first row
+  int dst[CPT];  // byte offset in the LDS tile (-1: no chunk for this thread)
+  __device__ void init(int tid) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ch = tid + u * NT;
+      if (ch < T::CHUNKS) {
+        const int R = ch / T::CPR, p = ch % T::CPR;
+        src[u] = T::perm(R) * T::ROWB + ((p ^ T::swz(R)) << 4);
+        dst[u] = ch * 16;
+      } else {
+        src[u] = 0;
+        dst[u] = -1;
+      }
+    }
+  }
+};
+
+// Buffer descriptor for rows [row0, rows) of a [rows, D] bf16 head: reads
+// past the last row return zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* head, int row0,
+                                                            int rows) {
+  const int left = rows - row0;
+  const uint32_t bytes = left > 0 ? (uint32_t)left * (uint32_t)(2 * D) : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)row0 * D), (short)0,
+                                           (int)bytes, kBufferRsrcWord3);
+}
+
+// Per-lane LDS offsets of the two fragment kinds read from a Tile.
+template <int D>
+struct FragAddr {
+  using T = Tile<D>;
+  int row;               // row fragment: row (lane%32), chunk base
+  int sw;                // swz of that row
+  int tr_lo[T::DBLK];    // transposed fragment, rows +0..3 of each 8
+  int tr_hi[T::DBLK];    // transposed fragment, rows +4..7
+  __device__ void init(int lane) {
+    const int r32 = lane & 31;
+    row = r32 * T::ROWB;
+    sw = T::swz(r32);
+    // ds_read_b64_tr_b16: in 16-lane group G, lane 4*jj + cc addresses row
+    // jj of a 4-row block and columns 4*cc .. 4*cc+3 of the group's 16-column
+    // slice; output lane i then holds column i of the four rows. Lanes
+    // l < 32 supply contraction rows 0..7 of a 16-row step, lanes >= 32 rows
+    // 8..15; in the permuted tile the source rows 16*gg + 8*t + c (c < 4) of
+    // a 32-row block sit at LDS rows 16*t + 4*gg + c, and rows
+    // 16*gg + 8*t + 4 + c at 16*t + 8 + 4*gg + c.
+    const int G = lane >> 4, L16 = lane & 15, jj = L16 >> 2, cc = L16 & 3;
+    const int gg = G >> 1, nh = G & 1;
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b) {
+      const int chunk = 4 * b + 2 * nh + (cc >> 1);
+      const int r_lo = 4 * gg + jj, r_hi = 8 + 4 * gg + jj;
+      tr_lo[b] = r_lo * T::ROWB + ((chunk ^ T::swz(r_lo)) << 4) + (cc & 1) * 8;
+      tr_hi[b] = r_hi * T::ROWB + ((chunk ^ T::swz(r_hi)) << 4) + (cc & 1) * 8;
+    }
+  }
+  // A operand: rows blk*32 + (lane%32), d = 16*t + 8*(lane/32) .. +7.
+  __device__ bf16x8_t row_frag(const unsigned char* tile, int blk, int t, int g) const {
+    const u32x4_t x = *(const u32x4_t*)(tile + blk * 32 * T::ROWB + row +
+                                        (((2 * t + g) ^ sw) << 4));
+    return __builtin_bit_cast(bf16x8_t, x);
+  }
+  // A operand of a transposed product: d = 32*b + (lane%32) by the 16
+  // source rows blk*32 + 16*(lane/32) + 8*t .. +7 (matching accumulator
+  // registers 8t .. 8t+7 of the permuted rows).
+  __device__ bf16x8_t tr_frag(const unsigned char* tile, int b, int blk, int t) const {
+    const unsigned char* base = tile + (blk * 32 + 16 * t) * T::ROWB;
+    const s16x4_t lo = lds_read_tr16(base + tr_lo[b]);
+    const s16x4_t hi = lds_read_tr16(base + tr_hi[b]);
+    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+// Row x of a [rows, D] bf16 head as the B operand of QSTEPS products:
+// step t holds d = 16*t + 8*g .. +7 (zeros past the last row).
+template <int D>
+__device__ __forceinline__ void load_b_rows(const uint16_t* head, int x, int rows, int g,
+                                            bf16x8_t* f) {
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (x < rows) w = *(const u32x4_t*)(head + (size_t)x * D + t * 16 + g * 8);
+    f[t] = __builtin_bit_cast(bf16x8_t, w);
+  }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Store 16 accumulator registers of a transposed (d by row) product: lane
+// holds d = 32*b + 8*i4 + 4*g + (0..3) of its row, times `mul`, as bf16.
+template <int D>
+__device__ __forceinline__ void store_rowT(uint16_t* row, const f32x16_t* acc, int g,
+                                           float mul) {
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = b * 32 + i4 * 8 + g * 4;
+      u32x2_t st;
+      st[0] = pack_bf16x2(acc[b][i4 * 4 + 0] * mul, acc[b][i4 * 4 + 1] * mul);
+      st[1] = pack_bf16x2(acc[b][i4 * 4 + 2] * mul, acc[b][i4 * 4 + 3] * mul);
+      *(u32x2_t*)(row + d0) = st;
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- dQ kernel
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqWaves * 64, 1) void attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const float* __restrict__ lse, const uint16_t* __restrict__ dout,
+    uint16_t* __restrict__ dq, float* __restrict__ delta, int M, int N, int tiles_m,
+    int heads, float c, float scale) {
+  using T = Tile<D>;
+  constexpr int NT = kDqWaves * 64, BM = kDqWaves * 32, BN = kTileRows;
+  constexpr int QSTEPS = T::QSTEPS, DBLK = T::DBLK;
+  // K ring (2), then V ring (2).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * T::BYTES];
+
+  const int tid = workitem_id();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, g = lane >> 5;
+
+  const TileId tile = tile_order(workgroup_id(), tiles_m, heads, CAUSAL);
+  const int bh = tile.bh;
+  const int q_wg0 = tile.tm * BM;
+  const int qw0 = q_wg0 + wave * 32;
+  const int qi = qw0 + r32;
+
+  const size_t q_off = (size_t)bh * M * D, kv_off = (size_t)bh * N * D;
+  const uint16_t* kh = k + kv_off;
+  const uint16_t* vh = v + kv_off;
+
+  int nt = (N + BN - 1) / BN;
+  if (CAUSAL) nt = min(nt, (min(q_wg0 + BM, M) - 1) / BN + 1);
+
+  Stager<D, NT> st;
+  st.init(tid);
+  FragAddr<D> fa;
+  fa.init(lane);
+  u32x4_t kst[Stager<D, NT>::CPT], vst[Stager<D, NT>::CPT];
+  auto load = [&](int j) {
+    const auto rk = rows_rsrc<D>(kh, j * BN, N);
+    const auto rv = rows_rsrc<D>(vh, j * BN, N);
+#pragma unroll
+    for (int u = 0; u < Stager<D, NT>::CPT; ++u) {
+      kst[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, st.src[u], 0, 0);
+      vst[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, st.src[u], 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < Stager<D, NT>::CPT; ++u)
+      if (st.dst[u] >= 0) {
+        *(u32x4_t*)(smem + buf * T::BYTES + st.dst[u]) = kst[u];
+        *(u32x4_t*)(smem + (2 + buf) * T::BYTES + st.dst[u]) = vst[u];
+      }
+  };
+
+  // Q^T and dO^T as B operands; delta_i = O_i . dO_i from the same layout.
+  bf16x8_t qf[QSTEPS], gf[QSTEPS];
+  load_b_rows<D>(q + q_off, qi, M, g, qf);
+  load_b_rows<D>(dout + q_off, qi, M, g, gf);
+  float dl;
+  {
+    bf16x8_t of[QSTEPS];
+    load_b_rows<D>(o + q_off, qi, M, g, of);
+    float part = 0.0f;
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) {
+      const u32x4_t ow = __builtin_bit_cast(u32x4_t, of[t]);
+      const u32x4_t gw = __builtin_bit_cast(u32x4_t, gf[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = fmaf(bf16_lo(ow[e]), bf16_lo(gw[e]), part);
+        part = fmaf(bf16_hi(ow[e]), bf16_hi(gw[e]), part);
+      }
+    }
+    dl = half_pair_sum(part);
+  }
+  float l2 = 0.0f;
+  if (qi < M) {
+    l2 = lse[(size_t)bh * M + qi] * kLog2e;
+    if (g == 0) delta[(size_t)bh * M + qi] = dl;
+  }
+
+  f32x16_t acc[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+
+  if (nt > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nt) load(j + 1);
+    const unsigned char* kt = smem + buf * T::BYTES;
+    const unsigned char* vt = smem + (2 + buf) * T::BYTES;
+
+    // S^T = K Q^T, dP^T = V dO^T: key block kb, lane's keys 16g + r.
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = 0.0f;
+        dp[kb][i] = 0.0f;
+      }
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma_32x32x16_bf16(fa.row_frag(kt, kb, t, g), qf[t], s[kb]);
+        dp[kb] = mfma_32x32x16_bf16(fa.row_frag(vt, kb, t, g), gf[t], dp[kb]);
+      }
+
+    // P^T = exp2(c s - log2e L), dS^T = P^T (dP^T - delta); masked keys give
+    // P = 0. Rounded to bf16: the B operand of dQ^T += K^T dS^T.
+    const int key0 = j * BN;
+    const bool masked = (key0 + BN > N) || (CAUSAL && key0 + BN - 1 > qw0);
+    u32x4_t ds[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i0 = t * 8 + 2 * e;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i0], c, -l2));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + 1], c, -l2));
+          if (masked) {
+            const int key = key0 + kb * 32 + g * 16 + i0;
+            if (key >= N || (CAUSAL && key > qi)) p0 = 0.0f;
+            if (key + 1 >= N || (CAUSAL && key + 1 > qi)) p1 = 0.0f;
+          }
+          ds[kb][t][e] = pack_bf16x2(p0 * (dp[kb][i0] - dl), p1 * (dp[kb][i0 + 1] - dl));
+        }
+
+    // dQ^T += K^T dS^T over the tile's four 16-key steps.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+          acc[b] = mfma_32x32x16_bf16(fa.tr_frag(kt, b, kb, t),
+                                      __builtin_bit_cast(bf16x8_t, ds[kb][t]), acc[b]);
+
+    if (j + 1 < nt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qi < M) store_rowT<D>(dq + q_off + (size_t)qi * D, acc, g, scale);
+}
+
+// ------------------------------------------------------------ dK/dV kernel
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDkvWaves * 64, 1) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ lse,
+    const float* __restrict__ delta, const uint16_t* __restrict__ dout,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int M, int N, int tiles_n,
+    int heads, float c, float scale) {
+  using T = Tile<D>;
+  constexpr int NT = kDkvWaves * 64, BNK = kDkvWaves * 32, BQ = kTileRows;
+  constexpr int QSTEPS = T::QSTEPS, DBLK = T::DBLK;
+  // Q ring (2), dO ring (2), then per-row log2e*L and delta (2 x 2 x 64).
+  constexpr int STAT_OFF = 4 * T::BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * T::BYTES + 4 * BQ * 4];
+
+  const int tid = workitem_id();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, g = lane >> 5;
+
+  // Under the causal mask the first key tiles see the most query rows: run
+  // them first (tile_order runs the last tile index first).
+  const TileId tile = tile_order(workgroup_id(), tiles_n, heads, CAUSAL);
+  const int bh = tile.bh;
+  const int tn = CAUSAL ? tiles_n - 1 - tile.tm : tile.tm;
+  const int k_wg0 = tn * BNK;
+  const int kw0 = k_wg0 + wave * 32;
+  const int kj = kw0 + r32;  // this lane's key row
+
+  const size_t q_off = (size_t)bh * M * D, kv_off = (size_t)bh * N * D;
+  const uint16_t* qh = q + q_off;
+  const uint16_t* gh = dout + q_off;
+  const float* lh = lse + (size_t)bh * M;
+  const float* dh = delta + (size_t)bh * M;
+
+  // Query tiles that can see a key of this workgroup.
+  const int t_end = (M + BQ - 1) / BQ;
+  const int t_beg = CAUSAL ? min(k_wg0 / BQ, t_end) : 0;
+
+  Stager<D, NT> st;
+  st.init(tid);
+  FragAddr<D> fa;
+  fa.init(lane);
+  constexpr int CPT = Stager<D, NT>::CPT;
+  u32x4_t qst[CPT], gst[CPT];
+  float stat = 0.0f;  // threads 0..63: log2e*L of a row; 64..127: delta
+  auto load = [&](int j) {
+    const auto rq = rows_rsrc<D>(qh, j * BQ, M);
+    const auto rg = rows_rsrc<D>(gh, j * BQ, M);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      qst[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, st.src[u], 0, 0);
+      gst[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, st.src[u], 0, 0);
+    }
+    if (tid < 2 * BQ) {
+      const int r = j * BQ + (tid & (BQ - 1));
+      // Rows past the end: P = exp2(-inf) = 0 and delta = 0.
+      if (tid < BQ) stat = r < M ? lh[r] * kLog2e : INFINITY;
+      else stat = r < M ? dh[r] : 0.0f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      if (st.dst[u] >= 0) {
+        *(u32x4_t*)(smem + buf * T::BYTES + st.dst[u]) = qst[u];
+        *(u32x4_t*)(smem + (2 + buf) * T::BYTES + st.dst[u]) = gst[u];
+      }
+    if (tid < 2 * BQ) ((float*)(smem + STAT_OFF))[buf * 2 * BQ + tid] = stat;
+  };
+
+  // K^T and V^T as B operands (lane's key row).
+  bf16x8_t kf[QSTEPS], vf[QSTEPS];
+  load_b_rows<D>(k + kv_off, kj, N, g, kf);
+  load_b_rows<D>(v + kv_off, kj, N, g, vf);
+
+  f32x16_t dka[DBLK], dva[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dka[b][i] = 0.0f;
+      dva[b][i] = 0.0f;
+    }
+
+  if (t_beg < t_end) {
+    load(t_beg);
+    store(0);
+  }
+  __syncthreads();
+  for (int j = t_beg; j < t_end; ++j) {
+    const int buf = (j - t_beg) & 1;
+    if (j + 1 < t_end) load(j + 1);
+    const unsigned char* qt = smem + buf * T::BYTES;
+    const unsigned char* gt = smem + (2 + buf) * T::BYTES;
+    const float* lt = (const float*)(smem + STAT_OFF) + buf * 2 * BQ;
+    const float* dt = lt + BQ;
+    const int q0 = j * BQ;
+    const bool masked = CAUSAL && q0 < kw0 + 31;
+
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // S = Q K^T and dP = dO V^T for query block qb: lane's queries
+      // q0 + 32 qb + 16 g + r, key kj.
+      f32x16_t s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.0f;
+        dp[i] = 0.0f;
+      }
+#pragma unroll
+      for (int t = 0; t < QSTEPS; ++t) {
+        s = mfma_32x32x16_bf16(fa.row_frag(qt, qb, t, g), kf[t], s);
+        dp = mfma_32x32x16_bf16(fa.row_frag(gt, qb, t, g), vf[t], dp);
+      }
+      const int qr0 = qb * 32 + 16 * g;  // first of the lane's 16 rows in the tile
+      u32x4_t pb[2], dsb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f32x4_t la = *(const f32x4_t*)(lt + qr0 + 8 * t);
+        const f32x4_t lb = *(const f32x4_t*)(lt + qr0 + 8 * t + 4);
+        const f32x4_t da = *(const f32x4_t*)(dt + qr0 + 8 * t);
+        const f32x4_t db = *(const f32x4_t*)(dt + qr0 + 8 * t + 4);
+        const float lv[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
+        const float dv8[8] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i0 = t * 8 + 2 * e;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[i0], c, -lv[2 * e]));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[i0 + 1], c, -lv[2 * e + 1]));
+          if (masked) {
+            const int qq = q0 + qr0 + i0;
+            if (kj > qq) p0 = 0.0f;
+            if (kj > qq + 1) p1 = 0.0f;
+          }
+          pb[t][e] = pack_bf16x2(p0, p1);
+          dsb[t][e] = pack_bf16x2(p0 * (dp[i0] - dv8[2 * e]), p1 * (dp[i0 + 1] - dv8[2 * e + 1]));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row steps.
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b) {
+          dva[b] = mfma_32x32x16_bf16(fa.tr_frag(gt, b, qb, t),
+                                      __builtin_bit_cast(bf16x8_t, pb[t]), dva[b]);
+          dka[b] = mfma_32x32x16_bf16(fa.tr_frag(qt, b, qb, t),
+                                      __builtin_bit_cast(bf16x8_t, dsb[t]), dka[b]);
+        }
+    }
+
+    if (j + 1 < t_end) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (kj < N) {
+    store_rowT<D>(dv + kv_off + (size_t)kj * D, dva, g, 1.0f);
+    store_rowT<D>(dk + kv_off + (size_t)kj * D, dka, g, scale);
+  }
+}
+
+// ----------------------------------------------------------------- launch
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_d(const BwdLaunchArgs& a) {
+  const float c = a.scale * kLog2e;
+  const int heads = (int)a.BH;
+  if (a.M > 0) {
+    constexpr int BM = kDqWaves * 32;
+    const int tiles_m = (int)((a.M + BM - 1) / BM);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(tiles_m * heads)),
+                       dim3(kDqWaves * 64), 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
+                       a.lse, (const uint16_t*)a.dout, (uint16_t*)a.dq, a.delta, (int)a.M,
+                       (int)a.N, tiles_m, heads, c, a.scale);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  constexpr int BNK = kDkvWaves * 32;
+  const int tiles_n = (int)((a.N + BNK - 1) / BNK);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(tiles_n * heads)),
+                     dim3(kDkvWaves * 64), 0, a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.delta,
+                     (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.M,
+                     (int)a.N, tiles_n, heads, c, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const BwdLaunchArgs& a) {
+  switch (a.D) {
+    case 32: return a.causal ? launch_bwd_d<32, true>(a) : launch_bwd_d<32, false>(a);
+    case 64: return a.causal ? launch_bwd_d<64, true>(a) : launch_bwd_d<64, false>(a);
+    case 128: return a.causal ? launch_bwd_d<128, true>(a) : launch_bwd_d<128, false>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int bwd_dq_tile_rows() { return kDqWaves * 32; }
+int bwd_dkdv_tile_rows() { return kDkvWaves * 32; }
+
+}  // namespace mi355

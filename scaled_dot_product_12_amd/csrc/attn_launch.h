@@ -30,4 +30,29 @@ hipError_t launch_small(const LaunchArgs& a, bool bf16);
 int main_bf16_tile_rows();
 int main_f32_tile_rows();
 
+struct BwdLaunchArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B*H*M] workspace, written by the dQ kernel
+  int64_t BH;
+  int64_t M, N, D;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+// Backward (bf16, D in {32, 64, 128}): dQ kernel (also writes delta), then
+// the dK/dV kernel, both on a.stream.
+hipError_t launch_bwd_bf16(const BwdLaunchArgs& a);
+// Rows per workgroup of the two backward kernels (grid sizing checks).
+int bwd_dq_tile_rows();
+int bwd_dkdv_tile_rows();
+
 }  // namespace mi355

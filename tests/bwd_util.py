@@ -1,0 +1,104 @@
+"""Helpers for the backward GPU parity tests: run attn_fwd then attn_bwd on
+the GPU, run the fp64 gradient oracle on the same (exact bf16) inputs, and
+compare every element against a bound derived from the arithmetic.
+
+The bound (bf16 unit roundoff u = 2^-8, fp32 u32 = 2^-24, lambda = 8):
+each gradient element is a sum over n rows of terms a_i, and the kernels
+round each term's factor once to bf16 (P for dV, dS for dK and dQ) with
+errors that are independent between terms, so by Hoeffding's inequality the
+sum's error stays below lambda * u * sqrt(sum_i abar_i^2) except with
+probability 2 exp(-lambda^2 / 2) ~ 2.5e-14 per element. abar_i is the term's
+magnitude with every source of error in it:
+    dV_jd:  P_ij |dO_id|
+    dK_jd:  scale P_ij (|dP_ij| + |delta_i| + dabs_i) |q_id|
+    dQ_id:  scale P_ij (|dP_ij| + |delta_i|) |k_jd|
+where dabs_i = sum_d |O_id dO_id| bounds the error of delta_i taken from the
+bf16-rounded forward output (its own rounding and the forward's error, each
+at most u * dabs_i). In dQ that error is common to the whole row, so it is
+added coherently: 2 u scale dabs_i sum_j P_ij |k_jd|. fp32 accumulation adds
+lambda * sqrt(n) * u32 * sum_i abar_i, and rounding the result to bf16
+u * |ref|.
+"""
+import numpy as np
+import torch
+
+import oracle
+import scaled_dot_product_12_amd as attn
+
+U_BF16 = 2.0 ** -8
+U_F32 = 2.0 ** -24
+LAMBDA = 8.0
+
+
+def gpu_fwd_bwd(q, k, v, g, causal, scale):
+    """attn_fwd then attn_bwd on cuda:0; returns numpy fp64 (dq, dk, dv, delta)."""
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    o, lse = attn.attn_fwd(qd, kd, vd, is_causal=causal, scale=scale)
+    dq, dk, dv = attn.attn_bwd(qd, kd, vd, o, lse, gd, is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().double().numpy()
+    return f(dq), f(dk), f(dv), o, lse
+
+
+def head_bounds(q, k, v, g, scale, causal, refs):
+    """Per-element bounds for one head (2-D fp64 arrays q [M,D], k, v [N,D],
+    g [M,D]); refs = oracle (dq, dk, dv) of that head."""
+    M, N = q.shape[0], k.shape[0]
+    o_ref, l_ref = oracle.attn_fwd(q[None, None], k[None, None], v[None, None],
+                                   is_causal=causal, scale=scale)
+    O, L = o_ref[0, 0], l_ref[0, 0]
+    S = scale * (q @ k.T)
+    if causal:
+        S = np.where(np.tril(np.ones((M, N), dtype=bool)), S, -np.inf)
+    P = np.exp(S - L[:, None])
+    dP = g @ v.T
+    delta = (O * g).sum(-1)
+    dabs = np.abs(O * g).sum(-1)
+    dq_ref, dk_ref, dv_ref = refs
+    sc = abs(scale)
+
+    def bound(w, x, n, ref, coherent=0.0):
+        # element (a, d) = sum_i w[i, a] * x[i, d] with w, x >= 0
+        rss = np.sqrt((w * w).T @ (x * x))
+        s1 = w.T @ x
+        return (LAMBDA * U_BF16 * rss + LAMBDA * np.sqrt(n) * U_F32 * s1
+                + U_BF16 * np.abs(ref) + coherent)
+
+    b_dv = bound(P, np.abs(g), M, dv_ref)
+    wk = sc * P * (np.abs(dP) + np.abs(delta)[:, None] + dabs[:, None])
+    b_dk = bound(wk, np.abs(q), M, dk_ref)
+    wq = sc * P * (np.abs(dP) + np.abs(delta)[:, None])
+    coh = 2.0 * U_BF16 * sc * dabs[:, None] * (P @ np.abs(k))
+    b_dq = bound(wq.T, np.abs(k), N, dq_ref, coherent=coh)
+    return b_dq, b_dk, b_dv
+
+
+def check_heads(q, k, v, g, causal, scale, heads=None, label=""):
+    """GPU forward + backward on the full tensors; every element of the
+    listed heads (default: all) against the oracle within head_bounds."""
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    print(f"[bwd-parity] {label} {tuple(q.shape)} N={N} causal={causal} scale={scale}",
+          flush=True)
+    dq, dk, dv, _, _ = gpu_fwd_bwd(q, k, v, g, causal, scale)
+    for t in (dq, dk, dv):
+        assert np.isfinite(t).all(), "non-finite gradient"
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    refs = oracle.attn_bwd_heads(q, k, v, g, heads, is_causal=causal, scale=scale)
+    worst = {}
+    for (b, h), ref in zip(heads, refs):
+        f64 = lambda t: t[b, h].double().numpy()
+        bounds = head_bounds(f64(q), f64(k), f64(v), f64(g), scale, causal, ref)
+        for name, got, r, bd in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref, bounds):
+            err = np.abs(got[b, h] - r)
+            # a zero bound (every term zero, e.g. keys no query sees) needs
+            # an exact zero
+            with np.errstate(divide="ignore", invalid="ignore"):
+                rel = np.where(bd > 0, err / bd, np.where(err > 0, np.inf, 0.0))
+            ratio = float(rel.max(initial=0.0))
+            worst[name] = max(worst.get(name, 0.0), ratio)
+            assert ratio <= 1.0, (f"{label} head {(b, h)} {name}: max |err| / bound = "
+                                  f"{ratio:.3g} (max |err| {err.max():.3g})")
+    return worst

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
-         "attn_status_string"])
+         "attn_status_string", "attn_bwd", "attn_bwd_validate"])
 
 
 def test_library_exports_every_declared_symbol(hip_lib):
@@ -160,3 +160,77 @@ def test_python_wrapper_rejects_before_any_gpu_call(hip_lib):
     with pytest.raises(ValueError):
         hip_lib.attn_fwd(q.half(), q.half(), q.half())  # not a GPU tensor either
     assert hip_lib.default_scale(128) == ctypes.c_float(128 ** -0.5).value
+
+
+# ------------------------------------------------------------- attn_bwd
+def bval(hip_lib, B=2, H=3, M=100, N=70, D=64, scale=0.125, causal=0, dtype=BF16,
+         **over):
+    names = ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")
+    p = {n: A + i * SZ for i, n in enumerate(names)}
+    p.update(over)
+    return hip_lib.attn_bwd_validate(*(p[n] for n in names), B, H, M, N, D, scale,
+                                     causal, dtype)
+
+
+def test_bwd_valid_and_empty(hip_lib):
+    for D in (32, 64, 128):
+        for causal in (0, 1):
+            assert bval(hip_lib, D=D, causal=causal) == OK
+    assert bval(hip_lib, M=1, N=1) == OK
+    assert bval(hip_lib, M=0, N=5) == OK        # dK = dV = 0 to write
+    assert bval(hip_lib, B=0) == OK
+    assert bval(hip_lib, M=0, N=0) == OK
+    assert bval(hip_lib, B=0, q=None, dq=None) == OK  # nothing to do: no pointer needed
+    # inputs may alias one another
+    assert bval(hip_lib, k=A, v=A, o=A, dout=A) == OK
+
+
+def test_bwd_invalid(hip_lib):
+    assert bval(hip_lib, B=-1) == INVALID
+    assert bval(hip_lib, N=-1) == INVALID
+    assert bval(hip_lib, M=4, N=0) == INVALID
+    assert bval(hip_lib, D=0) == INVALID
+    assert bval(hip_lib, causal=2) == INVALID
+    assert bval(hip_lib, dtype=7) == INVALID
+    assert bval(hip_lib, scale=float("nan")) == INVALID
+    assert bval(hip_lib, scale=float("inf")) == INVALID
+    for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta"):
+        assert bval(hip_lib, **{n: None}) == INVALID, n
+        # no query rows: only the key-side buffers are used
+        expect = INVALID if n in ("k", "v", "dk", "dv") else OK
+        assert bval(hip_lib, M=0, N=5, **{n: None}) == expect, n
+
+
+def test_bwd_unsupported(hip_lib):
+    assert bval(hip_lib, dtype=FP32) == UNSUPPORTED
+    for D in (16, 8, 48, 256):
+        assert bval(hip_lib, D=D) == UNSUPPORTED, D
+    assert bval(hip_lib, M=1 << 31, N=10) == UNSUPPORTED   # M*D past 32 bits
+    assert bval(hip_lib, B=1 << 40, H=1 << 40) == UNSUPPORTED
+
+
+def test_bwd_misaligned(hip_lib):
+    # each tensor moved by 8 bytes, to an address no other buffer is near
+    for i, n in enumerate(("q", "k", "v", "o", "dout", "dq", "dk", "dv")):
+        assert bval(hip_lib, **{n: A + (20 + i) * SZ + 8}) == MISALIGNED, n
+    assert bval(hip_lib, lse=A + 4 * SZ + 2) == MISALIGNED
+    assert bval(hip_lib, delta=A + 9 * SZ + 2) == MISALIGNED
+    assert bval(hip_lib, lse=A + 4 * SZ + 4, delta=A + 9 * SZ + 4) == OK
+
+
+def test_bwd_overlaps(hip_lib):
+    # B=2, H=3, M=100, N=70, D=64 bf16: q/o/dout/dq 76800 B, k/v/dk/dv 53760 B,
+    # lse/delta 2400 B.
+    assert bval(hip_lib, dq=A) == INVALID               # dq on q
+    assert bval(hip_lib, dk=A + 2 * SZ + 53760 - 16) == INVALID  # dk tail over v
+    assert bval(hip_lib, dk=A + 2 * SZ + 53760) == OK   # dk right after v
+    assert bval(hip_lib, delta=A + 4 * SZ) == INVALID   # delta on lse
+    assert bval(hip_lib, dv=A + 7 * SZ + 16) == INVALID  # dv inside dk
+    assert bval(hip_lib, delta=A + 6 * SZ + 76800 - 4) == INVALID  # delta over dq's end
+    assert bval(hip_lib, dq=A + 5 * SZ) == INVALID      # dq on dout
+
+
+def test_bwd_python_wrapper_rejects_before_any_gpu_call(hip_lib):
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        hip_lib.attn_bwd(q, q, q, q, torch.zeros(1, 1, 8), q)   # CPU tensors

@@ -1,0 +1,110 @@
+"""GPU parity of the attention backward (attn_bwd, bf16) against the fp64
+gradient oracle, every element of the compared heads within the bound derived
+in bwd_util.py. Each case runs the GPU forward first and feeds its O and L to
+the backward, as a training step would."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scaled_dot_product_12_amd.inputs import make_dout, make_qkv
+
+from bwd_util import check_heads
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, M, N, D, seed):
+    q, k, v = make_qkv(B, H, M, N, D, "bf16", seed)
+    return q, k, v, make_dout(B, H, M, D, "bf16", seed)
+
+
+def _scale(D):
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("M,N", [(200, 200), (130, 300), (300, 77), (256, 128)])
+def test_bwd_parity(hip_lib, D, causal, M, N):
+    q, k, v, g = _inputs(1, 2, M, N, D, seed=M + N + D)
+    check_heads(q, k, v, g, causal, _scale(D), label=f"D{D}")
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (1, 200), (200, 1), (5, 3), (64, 64), (65, 129)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_small_and_ragged(hip_lib, M, N, causal):
+    q, k, v, g = _inputs(2, 1, M, N, 64, seed=7 * M + N)
+    check_heads(q, k, v, g, causal, _scale(64), label="ragged")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.5])
+def test_bwd_other_scales(hip_lib, scale):
+    q, k, v, g = _inputs(1, 2, 150, 180, 128, seed=31)
+    check_heads(q, k, v, g, True, scale, label="scale")
+
+
+def test_bwd_keys_no_query_sees_get_zeros(hip_lib):
+    """Causal with N > M: keys past the last query are visible to no row, so
+    their dK and dV are exactly zero (written over NaN-filled outputs)."""
+    q, k, v, g = _inputs(1, 2, 100, 400, 64, seed=41)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    o, lse = hip_lib.attn_fwd(qd, kd, vd, is_causal=True)
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    hip_lib.attn_bwd(qd, kd, vd, o, lse, gd, is_causal=True, out=(dq, dk, dv))
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all()
+    assert (dk[:, :, 100:] == 0).all() and (dv[:, :, 100:] == 0).all()
+    check_heads(q, k, v, g, True, _scale(64), label="N>M")
+
+
+def test_bwd_no_queries_zero_fills(hip_lib):
+    """M = 0: no query sees any key; dK = dV = 0 for every key row."""
+    dev = torch.device("cuda:0")
+    k = torch.randn(1, 2, 70, 64, device=dev).to(torch.bfloat16)
+    q = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
+    o, lse = torch.empty_like(q), torch.empty(1, 2, 0, device=dev)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(k, float("nan"))
+    hip_lib.attn_bwd(q, k, k, o, lse, q, out=(torch.empty_like(q), dk, dv))
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+
+
+def test_bwd_deterministic_and_delta(hip_lib):
+    """Two calls give identical bits (no atomics), and delta holds
+    rowsum(O * dO) of the bf16 forward output."""
+    q, k, v, g = _inputs(2, 2, 300, 300, 128, seed=51)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    o, lse = hip_lib.attn_fwd(qd, kd, vd, is_causal=True)
+    delta = torch.empty(2, 2, 300, device=dev)
+    a = hip_lib.attn_bwd(qd, kd, vd, o, lse, gd, is_causal=True, delta=delta)
+    b = hip_lib.attn_bwd(qd, kd, vd, o, lse, gd, is_causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    od, gdd = o.double().cpu(), gd.double().cpu()
+    ref = (od * gdd).sum(-1)
+    mag = (od * gdd).abs().sum(-1)
+    # fp32 accumulation of 128 exact products
+    assert ((delta.double().cpu() - ref).abs() <= 128 * 2.0 ** -24 * mag + 1e-30).all()
+
+
+def test_bwd_c4_shape_sampled_heads(hip_lib):
+    """bf16 B=4 H=16 M=N=4096 D=128 non-causal, the launch the benchmark
+    times; two whole heads against the oracle."""
+    q, k, v, g = _inputs(4, 16, 4096, 4096, 128, seed=4)
+    check_heads(q, k, v, g, False, _scale(128), heads=[(0, 0), (3, 15)], label="c4")
+
+
+def test_bwd_c5_shape_sampled_head(hip_lib):
+    """bf16 causal B=2 H=32 M=N=8192 D=128; one whole head (the last one)
+    against the oracle."""
+    q, k, v, g = _inputs(2, 32, 8192, 8192, 128, seed=5)
+    check_heads(q, k, v, g, True, _scale(128), heads=[(1, 31)], label="c5")
