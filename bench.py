@@ -11,7 +11,8 @@ Prints ONE JSON line with the metric (TFLOP/s with 4*B*H*M*N*D FLOPs, halved
 when causal), the roofline of the dominant kernel, the CPU oracle's rate on a
 bounded sample of the same workload, and the other workloads (fp32 single
 head, fp32 batch-96 non-causal / causal, the two axial passes, bf16 causal
-8192) as additional measurements.
+8192, and the backward at the two bf16 shapes, 10*B*H*M*N*D FLOPs) as
+additional measurements.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
                        [--no-cpu-baseline] [--workload c4]
@@ -200,6 +201,32 @@ def cpu_baseline(w, target_s):
                       f"spaced in each), fp64, {dt:.1f} s wall"}
 
 
+def bwd_flops(w) -> float:
+    """Backward FLOPs: five products of 2*B*H*M*N*D each (QK^T, dO V^T, P^T dO,
+    dS^T Q, dS K), i.e. 2.5x the forward's count; halved when causal."""
+    f = 10.0 * w.B * w.H * w.M * w.N * w.D
+    return f / 2 if w.causal else f
+
+
+def measure_bwd(w, steps, warmup):
+    """Average time of one attn_bwd call (dQ kernel + dK/dV kernel) on the
+    workload's tensors, with the forward's O and L and a seeded dO."""
+    import torch
+    import scaled_dot_product_12_amd as attn
+    from scaled_dot_product_12_amd.inputs import make_dout
+    fn_fwd, (q, k, v, o, lse) = gpu_setup(w)
+    fn_fwd()
+    g = make_dout(w.B, w.H, w.M, w.D, w.dtype, w.seed).to(q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+
+    def fn():
+        attn.attn_bwd(q, k, v, o, lse, g, is_causal=w.causal, scale=w.scale,
+                      out=(dq, dk, dv), delta=delta)
+    ms, _ = time_launches(fn, steps, warmup)
+    return ms, bwd_flops(w) / (ms * 1e-3) / 1e12
+
+
 def measure(w, steps, warmup, graph):
     fn, tensors = gpu_setup(w)
     ms, wall = time_launches(fn, steps, warmup, graph=graph)
@@ -253,6 +280,20 @@ def main():
                 "tflops": round(xtf, 3), "frac_compute_peak": round(xtf / xpeak, 4),
                 "gbs": round(xgbs, 1), "frac_hbm_peak": round(xgbs / PEAK_HBM_GBS, 4),
                 "timing": "HIP graph of %d calls" % steps if small else "%d calls" % steps,
+            }
+
+    if not a.no_extra:
+        for name in ("c4", "c5"):
+            x = WORKLOADS[name]
+            steps = max(5, min(30, int(4e12 / bwd_flops(x))))
+            print(f"[bench] backward {x.describe()}", file=sys.stderr, flush=True)
+            bms, btf = measure_bwd(x, steps, 3)
+            torch.cuda.empty_cache()
+            extra["bwd_" + name] = {
+                "workload": "backward (dQ, dK, dV) " + x.describe(),
+                "us_per_call": round(bms * 1e3, 3), "tflops": round(btf, 3),
+                "flops_per_call": bwd_flops(x), "frac_compute_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+                "timing": "%d calls" % steps,
             }
 
     cpu = None

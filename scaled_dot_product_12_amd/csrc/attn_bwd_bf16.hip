@@ -19,10 +19,13 @@
 //    second kernel. Per tile: S^T = K Q^T and dP^T = V dO^T (K, V rows from
 //    LDS, Q^T, dO^T in registers), P^T and dS^T in registers, then
 //    dQ^T += K^T dS^T with K^T read from LDS through ds_read_b64_tr_b16.
-//  * attn_bwd_dkdv_kernel: one workgroup = 4 waves = 128 key rows; loops over
-//    query tiles of 64 rows. Per tile: S = Q K^T, dP = dO V^T (Q, dO rows from
-//    LDS, K^T, V^T in registers), P and dS, then dV^T += dO^T P and
-//    dK^T += Q^T dS with dO^T, Q^T read transposed from LDS.
+//  * attn_bwd_dkdv_kernel: one workgroup = 4 waves = 128 key rows, one wave
+//    per SIMD (its dK^T, dV^T accumulators and K^T, V^T operands need ~360
+//    registers); loops over query tiles of 64 rows, staged straight from HBM
+//    into LDS. Per tile: S = Q K^T, dP = dO V^T (Q, dO rows from LDS, K^T, V^T
+//    in registers) for both 32-query halves, then per half P and dS, then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed from
+//    LDS.
 //  * All products are v_mfma_f32_32x32x16_bf16. Every staged tile is stored
 //    with its rows permuted so that the 16 accumulator registers of a lane
 //    are 16 consecutive rows of the tile: rounded to bf16 those registers are
@@ -52,7 +55,7 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
 constexpr int kDqWaves = 8;    // dQ kernel: 256 query rows per workgroup
-constexpr int kDkvWaves = 4;   // dK/dV kernel: 128 key rows per workgroup
+constexpr int kDkvWaves = 8;   // dK/dV kernel: 256 key rows per workgroup
 constexpr int kTileRows = 64;  // rows of a staged K/V (or Q/dO) tile
 
 // A staged 64-row tile of a [rows, D] bf16 tensor in LDS.
@@ -73,7 +76,14 @@ struct Tile {
     const int b = r & 31;
     return (r & ~31) + ((b >> 2) & 1) * 16 + (b >> 3) * 4 + (b & 3);
   }
-  __device__ static constexpr int swz(int r) { return (r & 15) & (CPR - 1); }
+  // Row reads touch 16 consecutive rows at one logical chunk, transposed
+  // reads 4 consecutive rows (from a multiple of 4) at 4 consecutive chunks;
+  // with 16 chunks per row, rotating the low row bits (4 (r & 3) + (r >> 2) & 3)
+  // gives both patterns 16 distinct bank positions. Narrower rows keep the
+  // plain r & (CPR - 1).
+  __device__ static constexpr int swz(int r) {
+    return CPR == 16 ? ((4 * (r & 3)) | ((r >> 2) & 3)) : (r & 15) & (CPR - 1);
+  }
 };
 
 // Staging of one tile by NT threads: thread chunk u is LDS chunk
@@ -170,6 +180,19 @@ __device__ __forceinline__ void load_b_rows(const uint16_t* head, int x, int row
     f[t] = __builtin_bit_cast(bf16x8_t, w);
   }
 }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes
+// lds_wave_base + 16*l (lds_wave_base must be wave-uniform).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_wave_base,
+                                          int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voffset, 0, 0, 0);
+}
+
+// Wait for this wave's outstanding vector-memory operations (including
+// buffer loads into LDS) to complete.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -358,10 +381,14 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void attn_bwd_dkdv_kernel(
     int heads, float c, float scale) {
   using T = Tile<D>;
   constexpr int NT = kDkvWaves * 64, BNK = kDkvWaves * 32, BQ = kTileRows;
+  static_assert(BQ == 64, "one wave loads the 64 per-row statistics of a tile");
   constexpr int QSTEPS = T::QSTEPS, DBLK = T::DBLK;
   // Q ring (2), dO ring (2), then per-row log2e*L and delta (2 x 2 x 64).
+  // Then the workgroup's V rows (row-major, swizzled, unpermuted), kept for
+  // the whole kernel: V^T is read from there as the B operand of dP.
   constexpr int STAT_OFF = 4 * T::BYTES;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * T::BYTES + 4 * BQ * 4];
+  constexpr int V_OFF = STAT_OFF + 4 * BQ * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + BNK * T::ROWB];
 
   const int tid = workitem_id();
   const int lane = tid & 63;
@@ -392,37 +419,55 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void attn_bwd_dkdv_kernel(
   FragAddr<D> fa;
   fa.init(lane);
   constexpr int CPT = Stager<D, NT>::CPT;
-  u32x4_t qst[CPT], gst[CPT];
   float stat = 0.0f;  // threads 0..63: log2e*L of a row; 64..127: delta
-  auto load = [&](int j) {
+  // Q and dO tiles go from HBM straight into LDS (buffer loads with the lds
+  // flag: lane l of a wave writes 16 bytes at the wave's base + 16 l, which
+  // is the staging order ch = tid + u*NT), so they need no registers; the
+  // per-row statistics pass through one register.
+  auto load = [&](int j, int buf) {
     const auto rq = rows_rsrc<D>(qh, j * BQ, M);
     const auto rg = rows_rsrc<D>(gh, j * BQ, M);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      qst[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, st.src[u], 0, 0);
-      gst[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, st.src[u], 0, 0);
+      const int wbase = (wave * 64 + u * NT) * 16;  // wave-uniform
+      if (wbase < T::BYTES) {
+        lds_dma16(rq, smem + buf * T::BYTES + wbase, st.src[u]);
+        lds_dma16(rg, smem + (2 + buf) * T::BYTES + wbase, st.src[u]);
+      }
     }
-    if (tid < 2 * BQ) {
-      const int r = j * BQ + (tid & (BQ - 1));
+    if (wave < 2) {  // wave 0: log2e*L, wave 1: delta of the tile's rows
+      const int r = j * BQ + lane;
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(wave == 0 ? lh : dh), (short)0,
+                                                        M * 4, kBufferRsrcWord3);
+      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, r * 4, 0, 0));
       // Rows past the end: P = exp2(-inf) = 0 and delta = 0.
-      if (tid < BQ) stat = r < M ? lh[r] * kLog2e : INFINITY;
-      else stat = r < M ? dh[r] : 0.0f;
+      stat = wave == 0 ? (r < M ? x * kLog2e : INFINITY) : x;
     }
   };
+  // Make this wave's tile loads and its statistic visible to the workgroup
+  // (the caller's barrier follows).
   auto store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u)
-      if (st.dst[u] >= 0) {
-        *(u32x4_t*)(smem + buf * T::BYTES + st.dst[u]) = qst[u];
-        *(u32x4_t*)(smem + (2 + buf) * T::BYTES + st.dst[u]) = gst[u];
-      }
-    if (tid < 2 * BQ) ((float*)(smem + STAT_OFF))[buf * 2 * BQ + tid] = stat;
+    if (wave < 2) ((float*)(smem + STAT_OFF))[buf * 2 * BQ + tid] = stat;
+    wait_vmem();
   };
 
-  // K^T and V^T as B operands (lane's key row).
-  bf16x8_t kf[QSTEPS], vf[QSTEPS];
+  // K^T as the B operand (lane's key row) in registers; V rows
+  // k_wg0 .. k_wg0 + BNK - 1 (zeros past the head) into LDS.
+  bf16x8_t kf[QSTEPS];
   load_b_rows<D>(k + kv_off, kj, N, g, kf);
-  load_b_rows<D>(v + kv_off, kj, N, g, vf);
+  {
+    constexpr int VCH = BNK * T::CPR;
+    static_assert(VCH % NT == 0, "V rows split evenly over the threads");
+    const auto rv = rows_rsrc<D>(v + kv_off, k_wg0, N);
+#pragma unroll
+    for (int u = 0; u < VCH / NT; ++u) {
+      const int ch = tid + u * NT;
+      const int R = ch / T::CPR, pp = ch % T::CPR;
+      *(u32x4_t*)(smem + V_OFF + ch * 16) = __builtin_amdgcn_raw_buffer_load_b128(
+          rv, R * T::ROWB + ((pp ^ T::swz(R)) << 4), 0, 0);
+    }
+  }
+  const unsigned char* v_row = smem + V_OFF + (wave * 32 + r32) * T::ROWB;
 
   f32x16_t dka[DBLK], dva[DBLK];
 #pragma unroll
@@ -433,72 +478,110 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void attn_bwd_dkdv_kernel(
       dva[b][i] = 0.0f;
     }
 
-  if (t_beg < t_end) {
-    load(t_beg);
-    store(0);
-  }
-  __syncthreads();
-  for (int j = t_beg; j < t_end; ++j) {
-    const int buf = (j - t_beg) & 1;
-    if (j + 1 < t_end) load(j + 1);
-    const unsigned char* qt = smem + buf * T::BYTES;
-    const unsigned char* gt = smem + (2 + buf) * T::BYTES;
-    const float* lt = (const float*)(smem + STAT_OFF) + buf * 2 * BQ;
+  // One 64-query tile, block by block (32 queries): S = Q K^T and
+  // dP = dO V^T, then P and dS, then dV^T += dO^T P and dK^T += Q^T dS. The
+  // second wave of the SIMD runs beside it. `mask` (tile-uniform) applies the
+  // causal diagonal.
+  auto tile_body = [&](const unsigned char* qt, const unsigned char* gt, const float* lt,
+                       int q0, bool mask) __attribute__((always_inline)) {
     const float* dt = lt + BQ;
-    const int q0 = j * BQ;
-    const bool masked = CAUSAL && q0 < kw0 + 31;
-
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      // S = Q K^T and dP = dO V^T for query block qb: lane's queries
-      // q0 + 32 qb + 16 g + r, key kj.
       f32x16_t s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s[i] = 0.0f;
         dp[i] = 0.0f;
       }
+      // fenced chunks, one MFMA each, operands read PF chunks ahead:
+      // chunk i is S step i/2 (even: Q rows, K^T) or dP step i/2 (odd: dO
+      // rows, V^T)
+      {
+        constexpr int PF = 2, NA = 2 * QSTEPS;
+        bf16x8_t fa_[PF + 1], fb_[PF + 1];
+        auto rd = [&](int i, bf16x8_t& x, bf16x8_t& y) {
+          x = fa.row_frag((i & 1) ? gt : qt, qb, i >> 1, g);
+          if (i & 1) {
+            const u32x4_t vw = *(const u32x4_t*)(v_row + (((2 * (i >> 1) + g) ^ fa.sw) << 4));
+            y = __builtin_bit_cast(bf16x8_t, vw);
+          } else {
+            y = kf[i >> 1];
+          }
+        };
 #pragma unroll
-      for (int t = 0; t < QSTEPS; ++t) {
-        s = mfma_32x32x16_bf16(fa.row_frag(qt, qb, t, g), kf[t], s);
-        dp = mfma_32x32x16_bf16(fa.row_frag(gt, qb, t, g), vf[t], dp);
+        for (int i = 0; i < PF; ++i) rd(i, fa_[i], fb_[i]);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          if (i + PF < NA) rd(i + PF, fa_[(i + PF) % (PF + 1)], fb_[(i + PF) % (PF + 1)]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i & 1) dp = mfma_32x32x16_bf16(fa_[i % (PF + 1)], fb_[i % (PF + 1)], dp);
+          else s = mfma_32x32x16_bf16(fa_[i % (PF + 1)], fb_[i % (PF + 1)], s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      const int qr0 = qb * 32 + 16 * g;  // first of the lane's 16 rows in the tile
+      const int qr0 = qb * 32 + 16 * g;  // lane's queries q0 + qr0 + r, r < 16
       u32x4_t pb[2], dsb[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const f32x4_t la = *(const f32x4_t*)(lt + qr0 + 8 * t);
-        const f32x4_t lb = *(const f32x4_t*)(lt + qr0 + 8 * t + 4);
-        const f32x4_t da = *(const f32x4_t*)(dt + qr0 + 8 * t);
-        const f32x4_t db = *(const f32x4_t*)(dt + qr0 + 8 * t + 4);
-        const float lv[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
-        const float dv8[8] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i0 = t * 8 + 2 * e;
-          float p0 = __builtin_amdgcn_exp2f(fmaf(s[i0], c, -lv[2 * e]));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(s[i0 + 1], c, -lv[2 * e + 1]));
-          if (masked) {
-            const int qq = q0 + qr0 + i0;
-            if (kj > qq) p0 = 0.0f;
-            if (kj > qq + 1) p1 = 0.0f;
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t la = *(const f32x4_t*)(lt + qr0 + 8 * t + 4 * h);
+          const f32x4_t da = *(const f32x4_t*)(dt + qr0 + 8 * t + 4 * h);
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int e = 2 * h + e2, i0 = t * 8 + 2 * e;
+            float p0 = __builtin_amdgcn_exp2f(fmaf(s[i0], c, -la[2 * e2]));
+            float p1 = __builtin_amdgcn_exp2f(fmaf(s[i0 + 1], c, -la[2 * e2 + 1]));
+            if (mask) {
+              const int qq = q0 + qr0 + i0;
+              p0 = kj > qq ? 0.0f : p0;
+              p1 = kj > qq + 1 ? 0.0f : p1;
+            }
+            pb[t][e] = pack_bf16x2(p0, p1);
+            dsb[t][e] = pack_bf16x2(p0 * (dp[i0] - da[2 * e2]), p1 * (dp[i0 + 1] - da[2 * e2 + 1]));
           }
-          pb[t][e] = pack_bf16x2(p0, p1);
-          dsb[t][e] = pack_bf16x2(p0 * (dp[i0] - dv8[2 * e]), p1 * (dp[i0 + 1] - dv8[2 * e + 1]));
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row steps.
+      {
+        // chunk i: step t = i / (2 DBLK), d block b, dV (even) or dK (odd)
+        constexpr int PF = 2, NC = 4 * DBLK;
+        bf16x8_t fr[PF + 1];
+        auto rd = [&](int i) {
+          const int t = i / (2 * DBLK), b = (i % (2 * DBLK)) >> 1;
+          return fa.tr_frag((i & 1) ? qt : gt, b, qb, t);
+        };
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < PF; ++i) fr[i] = rd(i);
 #pragma unroll
-        for (int b = 0; b < DBLK; ++b) {
-          dva[b] = mfma_32x32x16_bf16(fa.tr_frag(gt, b, qb, t),
-                                      __builtin_bit_cast(bf16x8_t, pb[t]), dva[b]);
-          dka[b] = mfma_32x32x16_bf16(fa.tr_frag(qt, b, qb, t),
-                                      __builtin_bit_cast(bf16x8_t, dsb[t]), dka[b]);
+        for (int i = 0; i < NC; ++i) {
+          if (i + PF < NC) fr[(i + PF) % (PF + 1)] = rd(i + PF);
+          const int t = i / (2 * DBLK), b = (i % (2 * DBLK)) >> 1;
+          __builtin_amdgcn_sched_barrier(0);
+          if (i & 1)
+            dka[b] = mfma_32x32x16_bf16(fr[i % (PF + 1)], __builtin_bit_cast(bf16x8_t, dsb[t]), dka[b]);
+          else
+            dva[b] = mfma_32x32x16_bf16(fr[i % (PF + 1)], __builtin_bit_cast(bf16x8_t, pb[t]), dva[b]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
+  };
 
+  if (t_beg < t_end) {
+    load(t_beg, 0);
+    store(0);
+  }
+  __syncthreads();
+  for (int j = t_beg; j < t_end; ++j) {
+    const int buf = (j - t_beg) & 1;
+    if (j + 1 < t_end) load(j + 1, buf ^ 1);
+    const unsigned char* qt = smem + buf * T::BYTES;
+    const unsigned char* gt = smem + (2 + buf) * T::BYTES;
+    const float* lt = (const float*)(smem + STAT_OFF) + buf * 2 * BQ;
+    const int q0 = j * BQ;
+    // Causal: one body with a tile-uniform mask flag (a second inlined copy
+    // of the body would not fit the register budget).
+    tile_body(qt, gt, lt, q0, CAUSAL && q0 < kw0 + 31);
     if (j + 1 < t_end) store(buf ^ 1);
     __syncthreads();
   }
