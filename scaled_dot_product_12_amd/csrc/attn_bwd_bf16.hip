@@ -252,23 +252,19 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void attn_bwd_dq_kernel(
   st.init(tid);
   FragAddr<D> fa;
   fa.init(lane);
-  u32x4_t kst[Stager<D, NT>::CPT], vst[Stager<D, NT>::CPT];
-  auto load = [&](int j) {
+  // K and V tiles go from HBM straight into LDS (buffer loads with the lds
+  // flag; lane l of a wave writes the wave's base + 16 l).
+  auto load = [&](int j, int buf) {
     const auto rk = rows_rsrc<D>(kh, j * BN, N);
     const auto rv = rows_rsrc<D>(vh, j * BN, N);
 #pragma unroll
     for (int u = 0; u < Stager<D, NT>::CPT; ++u) {
-      kst[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, st.src[u], 0, 0);
-      vst[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, st.src[u], 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < Stager<D, NT>::CPT; ++u)
-      if (st.dst[u] >= 0) {
-        *(u32x4_t*)(smem + buf * T::BYTES + st.dst[u]) = kst[u];
-        *(u32x4_t*)(smem + (2 + buf) * T::BYTES + st.dst[u]) = vst[u];
+      const int wbase = (wave * 64 + u * NT) * 16;  // wave-uniform
+      if (wbase < T::BYTES) {
+        lds_dma16(rk, smem + buf * T::BYTES + wbase, st.src[u]);
+        lds_dma16(rv, smem + (2 + buf) * T::BYTES + wbase, st.src[u]);
       }
+    }
   };
 
   // Q^T and dO^T as B operands; delta_i = O_i . dO_i from the same layout.
@@ -304,18 +300,19 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
 
-  if (nt > 0) {
-    load(0);
-    store(0);
-  }
+  if (nt > 0) load(0, 0);
+  wait_vmem();
   __syncthreads();
   for (int j = 0; j < nt; ++j) {
     const int buf = j & 1;
-    if (j + 1 < nt) load(j + 1);
+    if (j + 1 < nt) load(j + 1, buf ^ 1);
     const unsigned char* kt = smem + buf * T::BYTES;
     const unsigned char* vt = smem + (2 + buf) * T::BYTES;
 
-    // S^T = K Q^T, dP^T = V dO^T: key block kb, lane's keys 16g + r.
+    // S^T = K Q^T, dP^T = V dO^T: key block kb, lane's keys 16g + r. Fenced
+    // chunks of one MFMA, operands read PF chunks ahead; chunk i is key
+    // block (i >> 1) & 1 of d-step i >> 2, S (i even) or dP (i odd).
+    constexpr int PF = 2, NA = 4 * QSTEPS, NC = 4 * DBLK;
     f32x16_t s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -324,13 +321,21 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void attn_bwd_dq_kernel(
         s[kb][i] = 0.0f;
         dp[kb][i] = 0.0f;
       }
+    {
+      bf16x8_t fr[PF + 1];
+      auto rd = [&](int i) { return fa.row_frag((i & 1) ? vt : kt, (i >> 1) & 1, i >> 2, g); };
 #pragma unroll
-    for (int t = 0; t < QSTEPS; ++t)
+      for (int i = 0; i < PF; ++i) fr[i] = rd(i);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma_32x32x16_bf16(fa.row_frag(kt, kb, t, g), qf[t], s[kb]);
-        dp[kb] = mfma_32x32x16_bf16(fa.row_frag(vt, kb, t, g), gf[t], dp[kb]);
+      for (int i = 0; i < NA; ++i) {
+        if (i + PF < NA) fr[(i + PF) % (PF + 1)] = rd(i + PF);
+        const int kb = (i >> 1) & 1, t = i >> 2;
+        __builtin_amdgcn_sched_barrier(0);
+        if (i & 1) dp[kb] = mfma_32x32x16_bf16(fr[i % (PF + 1)], gf[t], dp[kb]);
+        else s[kb] = mfma_32x32x16_bf16(fr[i % (PF + 1)], qf[t], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
 
     // P^T = exp2(c s - log2e L), dS^T = P^T (dP^T - delta); masked keys give
     // P = 0. Rounded to bf16: the B operand of dQ^T += K^T dS^T.
@@ -346,25 +351,34 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void attn_bwd_dq_kernel(
           const int i0 = t * 8 + 2 * e;
           float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i0], c, -l2));
           float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + 1], c, -l2));
-          if (masked) {
-            const int key = key0 + kb * 32 + g * 16 + i0;
-            if (key >= N || (CAUSAL && key > qi)) p0 = 0.0f;
-            if (key + 1 >= N || (CAUSAL && key + 1 > qi)) p1 = 0.0f;
-          }
+          const int key = key0 + kb * 32 + g * 16 + i0;
+          p0 = masked && (key >= N || (CAUSAL && key > qi)) ? 0.0f : p0;
+          p1 = masked && (key + 1 >= N || (CAUSAL && key + 1 > qi)) ? 0.0f : p1;
           ds[kb][t][e] = pack_bf16x2(p0 * (dp[kb][i0] - dl), p1 * (dp[kb][i0 + 1] - dl));
         }
 
-    // dQ^T += K^T dS^T over the tile's four 16-key steps.
+    // dQ^T += K^T dS^T over the tile's four 16-key steps (chunk i: d block
+    // i % DBLK of key step i / DBLK).
+    {
+      bf16x8_t fr[PF + 1];
+      auto rd = [&](int i) {
+        const int kt_ = i / DBLK;
+        return fa.tr_frag(kt, i % DBLK, kt_ >> 1, kt_ & 1);
+      };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < PF; ++i) fr[i] = rd(i);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int b = 0; b < DBLK; ++b)
-          acc[b] = mfma_32x32x16_bf16(fa.tr_frag(kt, b, kb, t),
-                                      __builtin_bit_cast(bf16x8_t, ds[kb][t]), acc[b]);
+      for (int i = 0; i < NC; ++i) {
+        if (i + PF < NC) fr[(i + PF) % (PF + 1)] = rd(i + PF);
+        const int b = i % DBLK, kt_ = i / DBLK;
+        __builtin_amdgcn_sched_barrier(0);
+        acc[b] = mfma_32x32x16_bf16(fr[i % (PF + 1)],
+                                    __builtin_bit_cast(bf16x8_t, ds[kt_ >> 1][kt_ & 1]), acc[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 
-    if (j + 1 < nt) store(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
