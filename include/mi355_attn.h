@@ -1,5 +1,6 @@
 /*
- * mi355_attn.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward.
+ * mi355_attn.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward
+ * (attn_fwd) and its gradient (attn_bwd).
  *
  * The operation (FlashAttention-2 forward, as stated by "Extend Thunder with
  * CUDA-Python", Python reference section, and "Blackwell Attention Example",
@@ -25,9 +26,10 @@
  * device. The library allocates nothing, keeps no pointer after a call
  * returns, and has no mutable global state.
  *
- * Execution: attn_fwd enqueues its kernel on `stream` (a hipStream_t; NULL is
- * the null stream) and returns without synchronising. Faults inside the
- * kernel surface at the caller's next synchronisation. Calls are reentrant.
+ * Execution: attn_fwd and attn_bwd enqueue their kernels on `stream` (a
+ * hipStream_t; NULL is the null stream) and return without synchronising.
+ * Faults inside a kernel surface at the caller's next synchronisation. Calls
+ * are reentrant.
  *
  * Errors: every argument check happens before any HIP call; a call that fails
  * a check launches nothing and writes nothing.
