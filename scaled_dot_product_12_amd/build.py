@@ -64,6 +64,12 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # A kernel whose host-side launch stub was not emitted links without an
+    # error and only fails when the library is loaded; catch it here.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "_ZN5mi355" in l]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError(f"{tmp} has undefined library symbols: {missing[:4]}")
     os.replace(tmp, LIB)
     return LIB
 
