@@ -1,0 +1,119 @@
+"""PyTorch-facing entry points over the library's C ABI: a differentiable
+attention op and a drop-in for ``torch.nn.functional.scaled_dot_product_attention``.
+
+* ``attention(q, k, v, is_causal, scale)`` is a ``torch.autograd.Function``
+  whose forward is ``attn_fwd`` (saving q, k, v, O and L) and whose backward
+  is ``attn_bwd`` -- the shape of the autograd function in "Blackwell
+  Attention Example" (autograd function section).
+* ``sdpa_checker`` takes torch's SDPA arguments and says whether this library
+  implements that call, with the reason when it does not -- the checker of
+  "Extend Thunder with CUDA-Python" (registering the kernel as an
+  implementation of torch SDPA), extended to what the kernels here support
+  (the causal mask, bf16 and fp32 forward, bf16 backward).
+* ``scaled_dot_product_attention`` has torch's signature; it runs the
+  library's kernels when the checker accepts and raises NotImplementedError
+  with the checker's reason otherwise. There is no silent fallback to another
+  implementation.
+
+Inputs that are not contiguous are copied to contiguous [B, H, seq, D]
+tensors first (a layout copy by torch; every step of the attention itself
+runs in the library's kernels).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import attn_bwd, attn_fwd
+
+FWD_HEAD_DIMS = (16, 32, 64, 128)
+BWD_HEAD_DIMS = (32, 64, 128)
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, is_causal: bool, scale: Optional[float]):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = attn_fwd(q, k, v, is_causal=is_causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.is_causal, ctx.scale = is_causal, scale
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        if q.dtype != torch.bfloat16 or q.shape[-1] not in BWD_HEAD_DIMS:
+            raise NotImplementedError(
+                f"attention backward supports bf16 with head dim in {BWD_HEAD_DIMS}; "
+                f"got {q.dtype}, D={q.shape[-1]}")
+        dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), is_causal=ctx.is_causal,
+                              scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention_with_lse(q, k, v, is_causal: bool = False,
+                       scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(O, L) like ``attn_fwd``, differentiable in q, k, v through O."""
+    return _Attention.apply(q, k, v, bool(is_causal), scale)
+
+
+def attention(q, k, v, is_causal: bool = False, scale: Optional[float] = None) -> torch.Tensor:
+    """O = softmax(scale q k^T [+ causal mask]) v for [B, H, seq, D] GPU
+    tensors, differentiable in q, k, v (backward: bf16, D in 32/64/128)."""
+    return _Attention.apply(q, k, v, bool(is_causal), scale)[0]
+
+
+def sdpa_checker(query, key, value, attn_mask=None, dropout_p: float = 0.0,
+                 is_causal: bool = False, scale: Optional[float] = None,
+                 enable_gqa: bool = False) -> Tuple[bool, str]:
+    """(True, "") when ``scaled_dot_product_attention`` with these arguments
+    runs on this library, else (False, reason)."""
+    if attn_mask is not None:
+        return False, "an explicit attn_mask is not supported (use is_causal)"
+    if dropout_p != 0.0:
+        return False, "dropout is not supported"
+    if enable_gqa:
+        return False, "grouped-query attention is not supported"
+    for name, t in (("query", query), ("key", key), ("value", value)):
+        if not isinstance(t, torch.Tensor):
+            return False, f"{name} is not a tensor"
+        if t.device.type != "cuda":
+            return False, f"{name} is not on a GPU"
+        if t.dim() != 4:
+            return False, f"{name} must be 4-D [B, H, seq, D]"
+    if not (query.device == key.device == value.device):
+        return False, "query, key and value are on different devices"
+    if not (query.dtype == key.dtype == value.dtype):
+        return False, "query, key and value have different dtypes"
+    if query.dtype not in (torch.float32, torch.bfloat16):
+        return False, f"dtype {query.dtype} is not supported (float32 or bfloat16)"
+    B, H, M, D = query.shape
+    if key.shape[:2] != (B, H) or key.shape[3] != D or value.shape != key.shape:
+        return False, "key/value shapes do not match the query (same B, H, D; one N)"
+    if D not in FWD_HEAD_DIMS:
+        return False, f"head dim {D} is not supported ({FWD_HEAD_DIMS})"
+    if M > 0 and key.shape[2] == 0:
+        return False, "no keys"
+    if scale is not None and not math.isfinite(float(scale)):
+        return False, "scale is not finite"
+    wants_grad = torch.is_grad_enabled() and any(
+        t.requires_grad for t in (query, key, value))
+    if wants_grad and (query.dtype != torch.bfloat16 or D not in BWD_HEAD_DIMS):
+        return False, (f"the backward supports bf16 with head dim in {BWD_HEAD_DIMS} "
+                       f"(inputs require grad)")
+    return True, ""
+
+
+def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p: float = 0.0,
+                                 is_causal: bool = False, scale: Optional[float] = None,
+                                 enable_gqa: bool = False) -> torch.Tensor:
+    """torch's SDPA signature on this library's kernels (raises
+    NotImplementedError with the reason when they do not apply)."""
+    ok, why = sdpa_checker(query, key, value, attn_mask, dropout_p, is_causal, scale,
+                           enable_gqa)
+    if not ok:
+        raise NotImplementedError(f"scaled_dot_product_attention: {why}")
+    return attention(query, key, value, is_causal=is_causal, scale=scale)

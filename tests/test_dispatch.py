@@ -1,0 +1,117 @@
+"""The PyTorch-facing layer (scaled_dot_product_12_amd.dispatch): the SDPA
+checker's decisions (CPU), and on the GPU that the SDPA drop-in and the
+autograd op run exactly the C-ABI kernels (bit-identical results) with
+gradients within the derived bound of the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_12_amd.inputs import make_dout, make_qkv
+
+
+def _dispatch():
+    from scaled_dot_product_12_amd import dispatch
+    return dispatch
+
+
+def test_checker_rejections_on_cpu(hip_lib):
+    d = _dispatch()
+    q = torch.zeros(1, 2, 8, 64)
+    ok, why = d.sdpa_checker(q, q, q)
+    assert not ok and "GPU" in why
+    for kw, word in ((dict(attn_mask=torch.ones(8, 8)), "attn_mask"),
+                     (dict(dropout_p=0.1), "dropout"),
+                     (dict(enable_gqa=True), "grouped")):
+        ok, why = d.sdpa_checker(q, q, q, **kw)
+        assert not ok and word in why
+    with pytest.raises(NotImplementedError):
+        d.scaled_dot_product_attention(q, q, q)
+
+
+
+
+def _gpu(*ts):
+    return tuple(t.to("cuda:0") for t in ts)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sdpa_dropin_is_the_library_forward(hip_lib, dtype, causal):
+    d = _dispatch()
+    q, k, v = _gpu(*make_qkv(2, 3, 150, 200, 64, dtype, seed=61))
+    with torch.no_grad():
+        ok, why = d.sdpa_checker(q, k, v, is_causal=causal)
+        assert ok, why
+        o = d.scaled_dot_product_attention(q, k, v, is_causal=causal)
+        ref, _ = hip_lib.attn_fwd(q, k, v, is_causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+
+
+@pytest.mark.gpu
+def test_non_contiguous_views(hip_lib):
+    """[B, seq, H, D] storage viewed as [B, H, seq, D] (a transpose), the
+    common layout of model code: copied to contiguous, same result."""
+    d = _dispatch()
+    q, k, v = _gpu(*make_qkv(2, 3, 130, 130, 128, "bf16", seed=62))
+    qt, kt, vt = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+    assert not qt.is_contiguous()
+    with torch.no_grad():
+        a = d.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+        b = d.scaled_dot_product_attention(q, k, v, is_causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_is_the_library_backward(hip_lib, causal):
+    import oracle
+    from bwd_util import head_bounds
+    d = _dispatch()
+    q0, k0, v0 = make_qkv(1, 2, 190, 170, 128, "bf16", seed=63)
+    g0 = make_dout(1, 2, 190, 128, "bf16", seed=63)
+    q, k, v = (t.to("cuda:0").requires_grad_(True) for t in (q0, k0, v0))
+    g = g0.to("cuda:0")
+    o = d.attention(q, k, v, is_causal=causal)
+    o.backward(g)
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        ref_o, lse = hip_lib.attn_fwd(q, k, v, is_causal=causal)
+        ref = hip_lib.attn_bwd(q.detach(), k.detach(), v.detach(), ref_o, lse, g,
+                               is_causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), ref_o)
+    for got, r in zip((q.grad, k.grad, v.grad), ref):
+        assert torch.equal(got, r)
+    scale = float(np.float32(1.0 / math.sqrt(128)))
+    refs = oracle.attn_bwd(q0, k0, v0, g0, is_causal=causal, scale=scale)
+    for h in range(2):
+        f64 = lambda t: t[0, h].double().numpy()
+        bounds = head_bounds(f64(q0), f64(k0), f64(v0), f64(g0), scale, causal,
+                             tuple(x[0, h] for x in refs))
+        for got, r, bd in zip((q.grad, k.grad, v.grad), refs, bounds):
+            err = np.abs(got[0, h].float().cpu().double().numpy() - r[0, h])
+            assert (err <= bd).all()
+
+
+@pytest.mark.gpu
+def test_checker_on_gpu_tensors(hip_lib):
+    d = _dispatch()
+    q, k, v = _gpu(*make_qkv(1, 1, 8, 8, 16, "bf16", seed=64))
+    assert d.sdpa_checker(q, k, v)[0]                      # forward only: D = 16 is fine
+    q.requires_grad_(True)
+    ok, why = d.sdpa_checker(q, k, v)
+    assert not ok and "backward" in why                   # no D = 16 backward
+    with torch.no_grad():
+        assert d.sdpa_checker(q, k, v)[0]                  # no grad needed
+    qf, kf, vf = _gpu(*make_qkv(1, 1, 8, 8, 64, "fp32", seed=65))
+    qf.requires_grad_(True)
+    assert not d.sdpa_checker(qf, kf, vf)[0]               # no fp32 backward
+    q16 = qf.detach().half()
+    assert not d.sdpa_checker(q16, q16, q16)[0]            # fp16 inputs
+    ok, why = d.sdpa_checker(q.detach(), k, v, attn_mask=torch.ones(8, 8, device="cuda:0"))
+    assert not ok
