@@ -11,8 +11,8 @@ Prints ONE JSON line with the metric (TFLOP/s with 4*B*H*M*N*D FLOPs, halved
 when causal), the roofline of the dominant kernel, the CPU oracle's rate on a
 bounded sample of the same workload, and the other workloads (fp32 single
 head, fp32 batch-96 non-causal / causal, the two axial passes, bf16 causal
-8192, and the backward at the two bf16 shapes, 10*B*H*M*N*D FLOPs) as
-additional measurements.
+8192, the Blackwell example's two bench shapes, and the backward at three
+bf16 shapes, 10*B*H*M*N*D FLOPs) as additional measurements.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
                        [--no-cpu-baseline] [--workload c4]
@@ -264,7 +264,7 @@ def main():
 
     extra = {}
     if not a.no_extra:
-        for name in ("c1", "c2", "c2c", "c3r", "c3c", "c5"):
+        for name in ("c1", "c2", "c2c", "c3r", "c3c", "c5", "p64", "p128"):
             if name == w.name:
                 continue
             x = WORKLOADS[name]
@@ -283,7 +283,7 @@ def main():
             }
 
     if not a.no_extra:
-        for name in ("c4", "c5"):
+        for name in ("c4", "c5", "p64"):
             x = WORKLOADS[name]
             steps = max(5, min(30, int(4e12 / bwd_flops(x))))
             print(f"[bench] backward {x.describe()}", file=sys.stderr, flush=True)

@@ -81,8 +81,13 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 
 }  // namespace
 
-// Waves per workgroup: two per SIMD.
+// Waves per workgroup: 8 (256 query rows, two waves per SIMD) for D = 128;
+// 4 (128 rows) for smaller heads, whose lighter register use lets three
+// workgroups share a CU, i.e. three waves per SIMD to overlap the softmax of
+// one with the products of another.
 constexpr int kBf16Waves = 8;
+__host__ __device__ constexpr int bf16_waves(int D) { return D <= 64 ? 4 : kBf16Waves; }
+__host__ __device__ constexpr int bf16_blocks_per_cu(int D) { return D <= 64 ? 3 : 1; }
 
 template <int D, int WAVES>
 struct Bf16Cfg {
@@ -115,7 +120,7 @@ struct Bf16Cfg {
 };
 
 template <int D, int WAVES, bool CAUSAL, bool POS_SCALE>
-__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int M, int N, int tiles_m, int heads, float c) {
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_bf16_kernel(
 
 template <int D, bool CAUSAL, bool POS>
 static hipError_t launch_bf16_d(const LaunchArgs& a) {
-  constexpr int WAVES = kBf16Waves;
+  constexpr int WAVES = bf16_waves(D);
   constexpr int BM = WAVES * 32;
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const dim3 grid((unsigned)(tiles_m * a.BH));
@@ -562,6 +567,7 @@ hipError_t launch_main_bf16(const LaunchArgs& a) {
   }
 }
 
-int main_bf16_tile_rows() { return kBf16Waves * 32; }
+// (the smallest tile of any head dim: grid-size checks stay conservative)
+int main_bf16_tile_rows() { return bf16_waves(16) * 32; }
 
 }  // namespace mi355

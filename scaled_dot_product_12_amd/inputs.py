@@ -83,6 +83,13 @@ WORKLOADS: Dict[str, Workload] = {
                    note="long-sequence bf16"),
     "c5": Workload("c5", 2, 32, 8192, 8192, 128, "bf16", True, 5,
                    note="causal bf16, longer context"),
+    # The bench shapes of "Blackwell Attention Example" (main function):
+    # (z, h, n_ctx, head_dim) = (4, 32, 8192, 64) and (4, 32, 8192, 128),
+    # bf16, non-causal.
+    "p64": Workload("p64", 4, 32, 8192, 8192, 64, "bf16", False, 6,
+                    note="Blackwell example bench shape, head dim 64"),
+    "p128": Workload("p128", 4, 32, 8192, 8192, 128, "bf16", False, 7,
+                     note="Blackwell example bench shape, head dim 128"),
 }
 
 _DT = {"fp32": torch.float32, "bf16": torch.bfloat16}

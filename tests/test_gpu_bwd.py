@@ -108,3 +108,10 @@ def test_bwd_c5_shape_sampled_head(hip_lib):
     against the oracle."""
     q, k, v, g = _inputs(2, 32, 8192, 8192, 128, seed=5)
     check_heads(q, k, v, g, True, _scale(128), heads=[(1, 31)], label="c5")
+
+
+def test_bwd_p64_shape_sampled_head(hip_lib):
+    """bf16 B=4 H=32 M=N=8192 D=64 non-causal (the Blackwell example's bench
+    shape with head dim 64); one whole head against the oracle."""
+    q, k, v, g = _inputs(4, 32, 8192, 8192, 64, seed=6)
+    check_heads(q, k, v, g, False, _scale(64), heads=[(2, 17)], label="p64")

@@ -87,7 +87,7 @@ def test_workload_full(name):
         check_full(q, k, v, w.causal, w.scale, path=MAIN, label=name + "-main")
 
 
-@pytest.mark.parametrize("name", ["c4", "c5"])
+@pytest.mark.parametrize("name", ["c4", "c5", "p64", "p128"])
 def test_workload_sampled(name):
     w = WORKLOADS[name]
     q, k, v = workload_inputs(w)
