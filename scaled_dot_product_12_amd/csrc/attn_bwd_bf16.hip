@@ -26,6 +26,8 @@
 //    in registers) for both 32-query halves, then per half P and dS, then
 //    dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed from
 //    LDS.
+//  * For D <= 64 both kernels use 4-wave workgroups (128 rows), three per CU,
+//    so that three waves share each SIMD.
 //  * All products are v_mfma_f32_32x32x16_bf16. Every staged tile is stored
 //    with its rows permuted so that the 16 accumulator registers of a lane
 //    are 16 consecutive rows of the tile: rounded to bf16 those registers are
@@ -54,8 +56,10 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
 // format, no swizzle): loads past num_records return zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
-constexpr int kDqWaves = 8;    // dQ kernel: 256 query rows per workgroup
-constexpr int kDkvWaves = 8;   // dK/dV kernel: 256 key rows per workgroup
+// Waves per workgroup (32 rows each): 8 for D = 128 (two per SIMD); 4 for
+// smaller heads, three workgroups per CU (three waves per SIMD).
+__host__ __device__ constexpr int bwd_waves(int D) { return D <= 64 ? 4 : 8; }
+__host__ __device__ constexpr int bwd_blocks_per_cu(int D) { return D <= 64 ? 3 : 1; }
 constexpr int kTileRows = 64;  // rows of a staged K/V (or Q/dO) tile
 
 // A staged 64-row tile of a [rows, D] bf16 tensor in LDS.
@@ -218,14 +222,14 @@ __device__ __forceinline__ void store_rowT(uint16_t* row, const f32x16_t* acc, i
 
 // ---------------------------------------------------------------- dQ kernel
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kDqWaves * 64, 1) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const float* __restrict__ lse, const uint16_t* __restrict__ dout,
     uint16_t* __restrict__ dq, float* __restrict__ delta, int M, int N, int tiles_m,
     int heads, float c, float scale) {
   using T = Tile<D>;
-  constexpr int NT = kDqWaves * 64, BM = kDqWaves * 32, BN = kTileRows;
+  constexpr int NT = bwd_waves(D) * 64, BM = bwd_waves(D) * 32, BN = kTileRows;
   constexpr int QSTEPS = T::QSTEPS, DBLK = T::DBLK;
   // K ring (2), then V ring (2).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * T::BYTES];
@@ -387,14 +391,14 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void attn_bwd_dq_kernel(
 
 // ------------------------------------------------------------ dK/dV kernel
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kDkvWaves * 64, 1) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const float* __restrict__ delta, const uint16_t* __restrict__ dout,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int M, int N, int tiles_n,
     int heads, float c, float scale) {
   using T = Tile<D>;
-  constexpr int NT = kDkvWaves * 64, BNK = kDkvWaves * 32, BQ = kTileRows;
+  constexpr int NT = bwd_waves(D) * 64, BNK = bwd_waves(D) * 32, BQ = kTileRows;
   static_assert(BQ == 64, "one wave loads the 64 per-row statistics of a tile");
   constexpr int QSTEPS = T::QSTEPS, DBLK = T::DBLK;
   // Q ring (2), dO ring (2), then per-row log2e*L and delta (2 x 2 x 64).
@@ -612,20 +616,20 @@ static hipError_t launch_bwd_d(const BwdLaunchArgs& a) {
   const float c = a.scale * kLog2e;
   const int heads = (int)a.BH;
   if (a.M > 0) {
-    constexpr int BM = kDqWaves * 32;
+    constexpr int BM = bwd_waves(D) * 32;
     const int tiles_m = (int)((a.M + BM - 1) / BM);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(tiles_m * heads)),
-                       dim3(kDqWaves * 64), 0, a.stream, (const uint16_t*)a.q,
+                       dim3(bwd_waves(D) * 64), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
                        a.lse, (const uint16_t*)a.dout, (uint16_t*)a.dq, a.delta, (int)a.M,
                        (int)a.N, tiles_m, heads, c, a.scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr int BNK = kDkvWaves * 32;
+  constexpr int BNK = bwd_waves(D) * 32;
   const int tiles_n = (int)((a.N + BNK - 1) / BNK);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(tiles_n * heads)),
-                     dim3(kDkvWaves * 64), 0, a.stream, (const uint16_t*)a.q,
+                     dim3(bwd_waves(D) * 64), 0, a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.delta,
                      (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.M,
                      (int)a.N, tiles_n, heads, c, a.scale);
@@ -641,7 +645,8 @@ hipError_t launch_bwd_bf16(const BwdLaunchArgs& a) {
   }
 }
 
-int bwd_dq_tile_rows() { return kDqWaves * 32; }
-int bwd_dkdv_tile_rows() { return kDkvWaves * 32; }
+// (the smallest tiles of any head dim: grid-size checks stay conservative)
+int bwd_dq_tile_rows() { return bwd_waves(32) * 32; }
+int bwd_dkdv_tile_rows() { return bwd_waves(32) * 32; }
 
 }  // namespace mi355
