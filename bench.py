@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X published peaks.
-PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # fp32 (vector and MFMA)
 PEAK_HBM_GBS = 8000.0       # HBM3E
 
@@ -258,13 +258,13 @@ def main():
     del tensors
     torch.cuda.empty_cache()
     print(f"[bench] {ms*1e3:.1f} us/step {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    is_bf16 = w.dtype == "bf16"
-    peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_FP32_TFLOPS
+    half = w.dtype in ("bf16", "fp16")
+    peak = PEAK_BF16_TFLOPS if half else PEAK_FP32_TFLOPS
     traffic = stored_traffic(w.name)
 
     extra = {}
     if not a.no_extra:
-        for name in ("c1", "c2", "c2c", "c3r", "c3c", "c5", "p64", "p128"):
+        for name in ("c1", "c2", "c2c", "c3r", "c3c", "c5", "p64", "p128", "c4h"):
             if name == w.name:
                 continue
             x = WORKLOADS[name]
@@ -274,7 +274,7 @@ def main():
             xms, _, xtf, xgbs, xt = measure(x, steps, 3, graph=small)
             del xt
             torch.cuda.empty_cache()
-            xpeak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_FP32_TFLOPS
+            xpeak = PEAK_BF16_TFLOPS if x.dtype in ("bf16", "fp16") else PEAK_FP32_TFLOPS
             extra[name] = {
                 "workload": x.describe(), "us_per_call": round(xms * 1e3, 3),
                 "tflops": round(xtf, 3), "frac_compute_peak": round(xtf / xpeak, 4),
@@ -312,8 +312,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if is_bf16 else "fp32",
-        "data": "synthetic (seeded N(0,1), rounded to bf16)" if is_bf16 else "synthetic (seeded N(0,1))",
+        "dtype": w.dtype,
+        "data": (f"synthetic (seeded N(0,1), rounded to {w.dtype})" if half
+                 else "synthetic (seeded N(0,1))"),
         "config": {"workload": w.describe(), "B": w.B, "H": w.H, "M": w.M, "N": w.N,
                    "D": w.D, "causal": w.causal, "seed": w.seed,
                    "parallelism": "single GPU"},

@@ -19,8 +19,10 @@
  *
  * Layout: contiguous row-major. q and o are [B, H, M, D]; k and v are
  * [B, H, N, D]; lse is [B, H, M] fp32 (the reference's [.., M, 1] is the same
- * memory). q, k, v and o share one element type (MI355_ATTN_FP32 or
- * MI355_ATTN_BF16); lse is always fp32.
+ * memory). q, k, v and o share one element type (MI355_ATTN_FP32,
+ * MI355_ATTN_BF16 or MI355_ATTN_FP16); lse is always fp32. With 16-bit inputs
+ * both products accumulate in fp32 and P is rounded to the input type before
+ * the second one, as the Blackwell example does for its 16-bit inputs.
  *
  * Ownership: every pointer is caller-owned device memory on the current HIP
  * device. The library allocates nothing, keeps no pointer after a call
@@ -43,9 +45,13 @@
 extern "C" {
 #endif
 
-/* Element type of q, k, v and o. */
+/* Element type of q, k, v and o. fp16: the Blackwell example's main
+ * function describes its test as float16 (its calls pass bf16), and the
+ * Thunder page's native-kernel section proposes 16-bit floats. The forward
+ * accepts all three types, the backward bf16 only. */
 #define MI355_ATTN_FP32 0
 #define MI355_ATTN_BF16 1
+#define MI355_ATTN_FP16 2
 
 /* Status codes. */
 #define MI355_ATTN_OK                0 /* success (also: nothing to do)            */
@@ -72,7 +78,7 @@ extern "C" {
  *   scale      multiplier of q.k, finite; the pages' default is 1/sqrt(D)
  *              (the Python binding passes that when scale is None).
  *   is_causal  0 or 1; 1 masks key j > query i (top-left aligned).
- *   dtype      MI355_ATTN_FP32 or MI355_ATTN_BF16.
+ *   dtype      MI355_ATTN_FP32, MI355_ATTN_BF16 or MI355_ATTN_FP16.
  *   stream     hipStream_t to enqueue on (NULL: null stream).
  *
  * Returns MI355_ATTN_OK, or:

@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libmi355_attn.so")
 # Mirrors of the header's constants.
 MI355_ATTN_FP32 = 0
 MI355_ATTN_BF16 = 1
+MI355_ATTN_FP16 = 2
 MI355_ATTN_OK = 0
 MI355_ATTN_ERR_INVALID_ARG = 1
 MI355_ATTN_ERR_UNSUPPORTED = 2
@@ -105,7 +106,9 @@ def _dtype_code(t) -> int:
         return MI355_ATTN_FP32
     if t.dtype == torch.bfloat16:
         return MI355_ATTN_BF16
-    raise ValueError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return MI355_ATTN_FP16
+    raise ValueError(f"unsupported dtype {t.dtype}: use float32, bfloat16 or float16")
 
 
 def _check(q, k, v):

@@ -28,11 +28,15 @@ bool overlap(const void* p, int64_t n, const void* r, int64_t m) {
 
 bool small_fits(int64_t M, int64_t N, int64_t D) { return M <= 64 && N <= 64 && D <= 32; }
 
+bool known_dtype(int dtype) {
+  return dtype == MI355_ATTN_FP32 || dtype == MI355_ATTN_BF16 || dtype == MI355_ATTN_FP16;
+}
+
 int validate(const void* q, const void* k, const void* v, const void* o,
              const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
              int64_t D, float scale, int is_causal, int dtype) {
   if (B < 0 || H < 0 || M < 0 || D < 1) return MI355_ATTN_ERR_INVALID_ARG;
-  if (dtype != MI355_ATTN_FP32 && dtype != MI355_ATTN_BF16) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return MI355_ATTN_ERR_INVALID_ARG;
   if (is_causal != 0 && is_causal != 1) return MI355_ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return MI355_ATTN_ERR_INVALID_ARG;
   int64_t BH, rows;
@@ -78,7 +82,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dv, const float* delta, int64_t B, int64_t H, int64_t M,
                  int64_t N, int64_t D, float scale, int is_causal, int dtype) {
   if (B < 0 || H < 0 || M < 0 || N < 0 || D < 1) return MI355_ATTN_ERR_INVALID_ARG;
-  if (dtype != MI355_ATTN_FP32 && dtype != MI355_ATTN_BF16) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return MI355_ATTN_ERR_INVALID_ARG;
   if (is_causal != 0 && is_causal != 1) return MI355_ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return MI355_ATTN_ERR_INVALID_ARG;
   int64_t BH, q_rows, k_rows;
@@ -145,7 +149,7 @@ int attn_fwd_validate(const void* q, const void* k, const void* v, void* o,
 int attn_fwd_select_path(int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
                          int is_causal, int dtype) {
   if (B < 0 || H < 0 || M < 0 || N < 1 || !supported_d(D)) return -1;
-  if (dtype != MI355_ATTN_FP32 && dtype != MI355_ATTN_BF16) return -1;
+  if (!known_dtype(dtype)) return -1;
   if (is_causal != 0 && is_causal != 1) return -1;
   int64_t BH, rows;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, M, &rows)) return -1;
@@ -178,12 +182,15 @@ int attn_fwd_path(const void* q, const void* k, const void* v, void* o,
   a.scale = scale;
   a.causal = is_causal != 0;
   a.stream = (hipStream_t)stream;
-  const bool bf16 = dtype == MI355_ATTN_BF16;
   hipError_t err;
   if (path == MI355_ATTN_PATH_SMALL)
-    err = mi355::launch_small(a, bf16);
+    err = mi355::launch_small(a, dtype);
+  else if (dtype == MI355_ATTN_BF16)
+    err = mi355::launch_main_bf16(a);
+  else if (dtype == MI355_ATTN_FP16)
+    err = mi355::launch_main_f16(a);
   else
-    err = bf16 ? mi355::launch_main_bf16(a) : mi355::launch_main_f32(a);
+    err = mi355::launch_main_f32(a);
   return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 

@@ -15,6 +15,8 @@ typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 
 // log2(e) and ln(2) in fp32. The kernels run the softmax in base 2
 // (exp2 of log2(e)-scaled scores), the form used by the Blackwell attention
@@ -30,6 +32,11 @@ constexpr float kRescaleThreshold = 8.0f;
 __device__ __forceinline__ f32x16_t mfma_32x32x16_bf16(bf16x8_t a, bf16x8_t b,
                                                         f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16_f16(f16x8_t a, f16x8_t b,
+                                                       f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16_t mfma_32x32x2_f32(float a, float b,
@@ -58,6 +65,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t f = {lo, hi};
   const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
   return __builtin_bit_cast(uint32_t, b);
+}
+
+// Round two fp32 values to fp16 (nearest-even) and pack them, lo first.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  const f16x2_t h = __builtin_convertvector(f, f16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // Work-item and workgroup index from the hardware registers. The kernels are

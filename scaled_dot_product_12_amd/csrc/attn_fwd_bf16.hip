@@ -119,7 +119,38 @@ struct Bf16Cfg {
   __device__ static constexpr int swz_v(int r) { return (4 * (r & 3)) & (CPR - 1); }
 };
 
-template <int D, int WAVES, bool CAUSAL, bool POS_SCALE>
+// The two 16-bit input types differ only in the matrix instruction, the
+// rounding of P and of O, and the row-sum dot product.
+template <bool F16>
+struct Half16 {
+  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    if constexpr (F16)
+      return mfma_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c);
+    else
+      return mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                c);
+  }
+  // Round (p0, p1) to the input type, add the rounded pair to rs, return it packed.
+  __device__ static uint32_t round_sum(float p0, float p1, float& rs) {
+    const f32x2_t f = {p0, p1};
+    if constexpr (F16) {
+      const f16x2_t h = __builtin_convertvector(f, f16x2_t);
+      const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+      rs = __builtin_amdgcn_fdot2(h, one, rs, false);
+      return __builtin_bit_cast(uint32_t, h);
+    } else {
+      const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+      const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+      rs = __builtin_amdgcn_fdot2_f32_bf16(b, one, rs, false);
+      return __builtin_bit_cast(uint32_t, b);
+    }
+  }
+  __device__ static uint32_t pack(float lo, float hi) {
+    return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+  }
+};
+
+template <int D, int WAVES, bool CAUSAL, bool POS_SCALE, bool F16>
 __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
@@ -230,12 +261,13 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   }
 
   // Q^T as the B operand: lane holds Q[qi][t*16 + g*8 .. +7].
-  bf16x8_t qf[QSTEPS];
+  using H = Half16<F16>;
+  u32x4_t qf[QSTEPS];
 #pragma unroll
   for (int t = 0; t < QSTEPS; ++t) {
     u32x4_t x = {0u, 0u, 0u, 0u};
     if (qi < M) x = *(const u32x4_t*)(qh + (size_t)qi * D + t * 16 + g * 8);
-    qf[t] = __builtin_bit_cast(bf16x8_t, x);
+    qf[t] = x;
   }
 
   const float cc_scale = POS_SCALE ? c : 1.0f;
@@ -262,7 +294,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
       const int t = i >> 1, kb = i & 1;
       const u32x4_t fr =
           *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
-      s[kb] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr), qf[t], s[kb]);
+      s[kb] = H::mma(fr, qf[t], s[kb]);
     }
   };
 
@@ -281,8 +313,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
       const s16x4_t lo = lds_read_tr16(a0);
       const s16x4_t hi = lds_read_tr16(a1);
       const s16x8_t fr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[b] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr),
-                                  __builtin_bit_cast(bf16x8_t, p[kb][t]), acc[b]);
+      acc[b] = H::mma(__builtin_bit_cast(u32x4_t, fr), p[kb][t], acc[b]);
     }
   };
 
@@ -331,11 +362,10 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   };
 
   // Probabilities of one 32-key half of a tile: bf16 P (B-operand layout)
-  // and their row sum (of the rounded values, via v_dot2_f32_bf16 with 1s).
+  // and their row sum (of the rounded values, via a dot2 with 1s).
   auto tile_exp = [&](const f32x16_t& s, u32x4_t* p) -> float {
-    // The row sum is accumulated from each freshly rounded bf16 pair (not
-    // from elements extracted back out of the packed vector).
-    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    // The row sum is accumulated from each freshly rounded pair (not from
+    // elements extracted back out of the packed vector).
     float rs = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -344,10 +374,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
       for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t * 8 + 2 * e], cc_scale, -m_sub));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t * 8 + 2 * e + 1], cc_scale, -m_sub));
-        const f32x2_t f = {p0, p1};
-        const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
-        w[e] = __builtin_bit_cast(uint32_t, b);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(b, one, rs, false);
+        w[e] = H::round_sum(p0, p1, rs);
       }
       p[t] = w;
     }
@@ -393,7 +420,6 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
     constexpr int PPC = 16 / NF_QK;  // exponential pairs per chunk
     const unsigned char* kb_base = smem + ((j + 1) % C::KBUF) * TILEB + k_rd;
     const auto rk = tile_rsrc(kh, j + 2);
-    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -411,16 +437,12 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
         const int pr = i * PPC + q, kb = pr >> 3, t = (pr >> 2) & 1, e = pr & 3;
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][t * 8 + 2 * e], cc_scale, -m_sub));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][t * 8 + 2 * e + 1], cc_scale, -m_sub));
-        const f32x2_t f = {p0, p1};
-        const bf16x2_t bb = __builtin_convertvector(f, bf16x2_t);
-        p[kb][t][e] = __builtin_bit_cast(uint32_t, bb);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(bb, one, rs, false);
+        p[kb][t][e] = H::round_sum(p0, p1, rs);
       }
       // the vector work of the chunk is issued before the MFMA's operand
       // wait, so an LDS stall does not hold it back
       __builtin_amdgcn_sched_barrier(0);
-      sn[i & 1] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (KPF + 1)]), qf[i >> 1],
-                                     sn[i & 1]);
+      sn[i & 1] = H::mma(fr[i % (KPF + 1)], qf[i >> 1], sn[i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     return rs;
@@ -440,8 +462,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
       if (has_next && i < CPT)
         vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_src0 + v_src_off(i), 0, 0);
       const int b = i % DBLK, kt = i / DBLK;
-      acc[b] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i % (VPF + 1)]),
-                                  __builtin_bit_cast(bf16x8_t, p[kt >> 1][kt & 1]), acc[b]);
+      acc[b] = H::mma(__builtin_bit_cast(u32x4_t, fr[i % (VPF + 1)]), p[kt >> 1][kt & 1], acc[b]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (has_next && NF_PV < CPT) load_v(j + 1);  // (never: NF_PV >= CPT for every D)
@@ -529,43 +550,48 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
       const int d0 = b * 32 + i4 * 8 + g * 4;
       if (d0 < D) {
         u32x2_t st;
-        st[0] = pack_bf16x2(acc[b][i4 * 4 + 0] * inv, acc[b][i4 * 4 + 1] * inv);
-        st[1] = pack_bf16x2(acc[b][i4 * 4 + 2] * inv, acc[b][i4 * 4 + 3] * inv);
+        st[0] = H::pack(acc[b][i4 * 4 + 0] * inv, acc[b][i4 * 4 + 1] * inv);
+        st[1] = H::pack(acc[b][i4 * 4 + 2] * inv, acc[b][i4 * 4 + 3] * inv);
         *(u32x2_t*)(orow + d0) = st;
       }
     }
   if (g == 0) lse[(size_t)bh * M + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool POS>
-static hipError_t launch_bf16_d(const LaunchArgs& a) {
+template <int D, bool CAUSAL, bool POS, bool F16>
+static hipError_t launch_16_d(const LaunchArgs& a) {
   constexpr int WAVES = bf16_waves(D);
   constexpr int BM = WAVES * 32;
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const dim3 grid((unsigned)(tiles_m * a.BH));
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, WAVES, CAUSAL, POS>), grid,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, WAVES, CAUSAL, POS, F16>), grid,
                      dim3(WAVES * 64), 0, a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                      a.lse, (int)a.M, (int)a.N, tiles_m, (int)a.BH, a.scale * kLog2e);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_bf16_dispatch(const LaunchArgs& a) {
+template <int D, bool F16>
+static hipError_t launch_16_dispatch(const LaunchArgs& a) {
   const bool pos = a.scale > 0.0f;
-  if (a.causal) return pos ? launch_bf16_d<D, true, true>(a) : launch_bf16_d<D, true, false>(a);
-  return pos ? launch_bf16_d<D, false, true>(a) : launch_bf16_d<D, false, false>(a);
+  if (a.causal)
+    return pos ? launch_16_d<D, true, true, F16>(a) : launch_16_d<D, true, false, F16>(a);
+  return pos ? launch_16_d<D, false, true, F16>(a) : launch_16_d<D, false, false, F16>(a);
 }
 
-hipError_t launch_main_bf16(const LaunchArgs& a) {
+template <bool F16>
+static hipError_t launch_main_16(const LaunchArgs& a) {
   switch (a.D) {
-    case 16: return launch_bf16_dispatch<16>(a);
-    case 32: return launch_bf16_dispatch<32>(a);
-    case 64: return launch_bf16_dispatch<64>(a);
-    case 128: return launch_bf16_dispatch<128>(a);
+    case 16: return launch_16_dispatch<16, F16>(a);
+    case 32: return launch_16_dispatch<32, F16>(a);
+    case 64: return launch_16_dispatch<64, F16>(a);
+    case 128: return launch_16_dispatch<128, F16>(a);
     default: return hipErrorInvalidValue;
   }
 }
+
+hipError_t launch_main_bf16(const LaunchArgs& a) { return launch_main_16<false>(a); }
+hipError_t launch_main_f16(const LaunchArgs& a) { return launch_main_16<true>(a); }
 
 // (the smallest tile of any head dim: grid-size checks stay conservative)
 int main_bf16_tile_rows() { return bf16_waves(16) * 32; }

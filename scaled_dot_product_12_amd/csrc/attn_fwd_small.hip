@@ -25,7 +25,7 @@
 //     A = V^T,      lane supplies V[16 kb + 4 g + r][16 db + n]
 //     B = P^T,      lane supplies its own P for key 16 kb + 4 g + r
 //     result: lane holds O[q0 + n][16 db + 4 g + r], r < 4 -- one 16-byte
-//     (fp32) or 8-byte (bf16) store per block.
+//     (fp32) or 8-byte (bf16, fp16) store per block.
 
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -57,26 +57,37 @@ __device__ __forceinline__ float pair16_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Element types of q, k, v and o.
+constexpr int kEtF32 = 0, kEtBf16 = 1, kEtF16 = 2;
+
+// Two packed 16-bit elements widened to fp32 (exact for both types; bf16 bits
+// are the top half of the fp32 bits).
+template <int ET>
+__device__ __forceinline__ void widen2(uint32_t w, float* x) {
+  if (ET == kEtBf16) {
+    x[0] = __uint_as_float(w << 16);
+    x[1] = __uint_as_float(w & 0xffff0000u);
+  } else {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, w);
+    x[0] = (float)h[0];
+    x[1] = (float)h[1];
+  }
+}
+
 // Loads of n consecutive elements (n = 4 or 8) starting at element e,
-// widened to fp32. bf16 -> fp32 is exact (the bf16 bits are the top half).
-template <bool BF16, int NE>
+// widened to fp32.
+template <int ET, int NE>
 __device__ __forceinline__ void load_row_part(const void* base, size_t e, float* x) {
-  if (BF16) {
+  if (ET != kEtF32) {
     const uint16_t* p = (const uint16_t*)base + e;
     if (NE == 4) {
       const u32x2_t w = *(const u32x2_t*)p;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-      }
+      for (int i = 0; i < 2; ++i) widen2<ET>(w[i], x + 2 * i);
     } else {
       const u32x4_t w = *(const u32x4_t*)p;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-      }
+      for (int i = 0; i < 4; ++i) widen2<ET>(w[i], x + 2 * i);
     }
   } else {
     const float* p = (const float*)base + e;
@@ -88,14 +99,15 @@ __device__ __forceinline__ void load_row_part(const void* base, size_t e, float*
   }
 }
 
-template <bool BF16>
+template <int ET>
 __device__ __forceinline__ float load_one(const void* base, size_t e) {
-  if (BF16) return __uint_as_float((uint32_t)((const uint16_t*)base)[e] << 16);
+  if (ET == kEtBf16) return __uint_as_float((uint32_t)((const uint16_t*)base)[e] << 16);
+  if (ET == kEtF16) return (float)((const _Float16*)base)[e];
   return ((const float*)base)[e];
 }
 }  // namespace
 
-template <bool BF16, int D>
+template <int ET, int D>
 __global__ __launch_bounds__(kSmallQRows * 4 * 4) void attn_fwd_small_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv,
     const void* __restrict__ vv, void* __restrict__ ov, float* __restrict__ lse,
@@ -120,20 +132,20 @@ __global__ __launch_bounds__(kSmallQRows * 4 * 4) void attn_fwd_small_kernel(
   // ---- all loads up front (rows past the end are clamped; their scores are
   // masked, so the clamped values never reach the result).
   float qf[DQ];
-  load_row_part<BF16, DQ>(qv, q_off + (size_t)min(qi, M - 1) * D + g * DQ, qf);
+  load_row_part<ET, DQ>(qv, q_off + (size_t)min(qi, M - 1) * D + g * DQ, qf);
   float kf[kSmallMaxKB][DQ];
   float vf[kSmallMaxKB][DB][4];
 #pragma unroll
   for (int kb = 0; kb < kSmallMaxKB; ++kb) {
     if (kb < nkb) {
       const int kr = min(16 * kb + n, N - 1);
-      load_row_part<BF16, DQ>(kv, kv_off + (size_t)kr * D + g * DQ, kf[kb]);
+      load_row_part<ET, DQ>(kv, kv_off + (size_t)kr * D + g * DQ, kf[kb]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int vr = min(16 * kb + 4 * g + r, N - 1);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          vf[kb][db][r] = load_one<BF16>(vv, kv_off + (size_t)vr * D + 16 * db + n);
+          vf[kb][db][r] = load_one<ET>(vv, kv_off + (size_t)vr * D + 16 * db + n);
       }
     }
   }
@@ -186,10 +198,15 @@ __global__ __launch_bounds__(kSmallQRows * 4 * 4) void attn_fwd_small_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const size_t at = q_off + (size_t)qi * D + 16 * db + 4 * g;
-      if (BF16) {
+      if (ET == kEtBf16) {
         u32x2_t st;
         st[0] = pack_bf16x2(o[db][0] * rinv, o[db][1] * rinv);
         st[1] = pack_bf16x2(o[db][2] * rinv, o[db][3] * rinv);
+        *(u32x2_t*)((uint16_t*)ov + at) = st;
+      } else if (ET == kEtF16) {
+        u32x2_t st;
+        st[0] = pack_f16x2(o[db][0] * rinv, o[db][1] * rinv);
+        st[1] = pack_f16x2(o[db][2] * rinv, o[db][3] * rinv);
         *(u32x2_t*)((uint16_t*)ov + at) = st;
       } else {
         const f32x4_t st = o[db] * rinv;
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(kSmallQRows * 4 * 4) void attn_fwd_small_kernel(
   }
 }
 
-hipError_t launch_small(const LaunchArgs& a, bool bf16) {
+hipError_t launch_small(const LaunchArgs& a, int et) {
   if (a.M < 1 || a.M > kSmallMaxM || a.N < 1 || a.N > kSmallMaxN ||
       (a.D != 16 && a.D != 32))
     return hipErrorInvalidValue;
@@ -212,15 +229,18 @@ hipError_t launch_small(const LaunchArgs& a, bool bf16) {
   const dim3 block((unsigned)(64 * wph * hpw));
   const float c = a.scale * kLog2e;
   const int M = (int)a.M, N = (int)a.N, causal = (int)a.causal;
-#define MI355_SMALL_LAUNCH(BF, DD)                                                   \
-  hipLaunchKernelGGL((attn_fwd_small_kernel<BF, DD>), grid, block, 0, a.stream, a.q, \
+#define MI355_SMALL_LAUNCH(ET, DD)                                                   \
+  hipLaunchKernelGGL((attn_fwd_small_kernel<ET, DD>), grid, block, 0, a.stream, a.q, \
                      a.k, a.v, a.o, a.lse, M, N, causal, c, (int)a.BH, wph)
-  if (bf16) {
-    if (a.D == 16) MI355_SMALL_LAUNCH(true, 16);
-    else MI355_SMALL_LAUNCH(true, 32);
+  if (et == kEtBf16) {
+    if (a.D == 16) MI355_SMALL_LAUNCH(kEtBf16, 16);
+    else MI355_SMALL_LAUNCH(kEtBf16, 32);
+  } else if (et == kEtF16) {
+    if (a.D == 16) MI355_SMALL_LAUNCH(kEtF16, 16);
+    else MI355_SMALL_LAUNCH(kEtF16, 32);
   } else {
-    if (a.D == 16) MI355_SMALL_LAUNCH(false, 16);
-    else MI355_SMALL_LAUNCH(false, 32);
+    if (a.D == 16) MI355_SMALL_LAUNCH(kEtF32, 16);
+    else MI355_SMALL_LAUNCH(kEtF32, 32);
   }
 #undef MI355_SMALL_LAUNCH
   return hipGetLastError();

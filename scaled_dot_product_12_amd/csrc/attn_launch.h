@@ -22,9 +22,11 @@ struct LaunchArgs {
 
 // Tiled MFMA kernels with the online softmax (any M, N >= 1).
 hipError_t launch_main_bf16(const LaunchArgs& a);
+hipError_t launch_main_f16(const LaunchArgs& a);
 hipError_t launch_main_f32(const LaunchArgs& a);
-// One-tile LDS-resident kernel (M <= 64, N <= 64, D <= 32).
-hipError_t launch_small(const LaunchArgs& a, bool bf16);
+// One-tile register-resident kernel (M <= 64, N <= 64, D <= 32); et is the
+// element type: 0 fp32, 1 bf16, 2 fp16 (the ABI's dtype codes).
+hipError_t launch_small(const LaunchArgs& a, int et);
 
 // Query rows per workgroup of the main kernels (grid sizing checks).
 int main_bf16_tile_rows();

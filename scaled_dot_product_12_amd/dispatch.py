@@ -88,8 +88,8 @@ def sdpa_checker(query, key, value, attn_mask=None, dropout_p: float = 0.0,
         return False, "query, key and value are on different devices"
     if not (query.dtype == key.dtype == value.dtype):
         return False, "query, key and value have different dtypes"
-    if query.dtype not in (torch.float32, torch.bfloat16):
-        return False, f"dtype {query.dtype} is not supported (float32 or bfloat16)"
+    if query.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        return False, f"dtype {query.dtype} is not supported (float32, bfloat16 or float16)"
     B, H, M, D = query.shape
     if key.shape[:2] != (B, H) or key.shape[3] != D or value.shape != key.shape:
         return False, "key/value shapes do not match the query (same B, H, D; one N)"

@@ -5,8 +5,8 @@ them. Both the HIP path's tests/benchmark and the CPU oracle are fed from here.
 
 Recipe (every workload): ``g = torch.Generator("cpu").manual_seed(seed)``, then
 Q, K, V in that order, each ``torch.randn(shape, dtype=float32, generator=g)``.
-bf16 workloads round those fp32 draws to bf16 with ``.to(torch.bfloat16)``
-(round-to-nearest-even). The upstream gradient dO of a backward problem is
+bf16 (fp16) workloads round those fp32 draws with ``.to(torch.bfloat16)``
+(``.to(torch.float16)``), round-to-nearest-even. The upstream gradient dO of a backward problem is
 drawn the same way from its own generator, seeded with ``seed + DOUT_SEED_OFFSET``
 (so Q, K, V are the same draws as the forward problem's). Shapes follow the
 pages' workloads:
@@ -38,7 +38,7 @@ class Workload:
     M: int
     N: int
     D: int
-    dtype: str            # "fp32" or "bf16"
+    dtype: str            # "fp32", "bf16" or "fp16"
     causal: bool
     seed: int
     axial: str = ""       # "" or "row" / "col" for the axial passes
@@ -90,9 +90,13 @@ WORKLOADS: Dict[str, Workload] = {
                     note="Blackwell example bench shape, head dim 64"),
     "p128": Workload("p128", 4, 32, 8192, 8192, 128, "bf16", False, 7,
                      note="Blackwell example bench shape, head dim 128"),
+    # The long-sequence shape in fp16 (the Blackwell example's main function
+    # describes its test as float16): the same draws as c4, rounded to fp16.
+    "c4h": Workload("c4h", 4, 16, 4096, 4096, 128, "fp16", False, 4,
+                    note="long-sequence fp16"),
 }
 
-_DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+_DT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 
 def make_qkv(B: int, H: int, M: int, N: int, D: int, dtype: str = "fp32",

@@ -12,7 +12,7 @@ import torch
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mi355_attn.h")
 
-FP32, BF16 = 0, 1
+FP32, BF16, FP16 = 0, 1, 2
 OK, INVALID, UNSUPPORTED, MISALIGNED, HIPERR = 0, 1, 2, 3, 4
 
 
@@ -66,7 +66,7 @@ def val(hip_lib, *, q=None, k=None, v=None, o=None, lse=None, B=2, H=3, M=100,
 
 
 def test_valid_arguments(hip_lib):
-    for dtype in (FP32, BF16):
+    for dtype in (FP32, BF16, FP16):
         for D in (16, 32, 64, 128):
             for causal in (0, 1):
                 assert val(hip_lib, D=D, dtype=dtype, causal=causal) == OK
@@ -86,7 +86,8 @@ def test_invalid_arguments(hip_lib):
     assert val(hip_lib, D=0) == INVALID
     assert val(hip_lib, causal=2) == INVALID
     assert val(hip_lib, causal=-1) == INVALID
-    assert val(hip_lib, dtype=2) == INVALID
+    assert val(hip_lib, dtype=3) == INVALID
+    assert val(hip_lib, dtype=-1) == INVALID
     assert val(hip_lib, scale=float("inf")) == INVALID
     assert val(hip_lib, scale=float("nan")) == INVALID
 
@@ -134,6 +135,8 @@ def test_select_path(hip_lib):
     SMALL, MAIN = hip_lib.MI355_ATTN_PATH_SMALL, hip_lib.MI355_ATTN_PATH_MAIN
     assert f(128, 4, 32, 32, 16, 0, FP32) == SMALL   # axial pass
     assert f(1, 1, 64, 64, 32, 1, BF16) == SMALL
+    assert f(128, 4, 32, 32, 16, 0, FP16) == SMALL
+    assert f(4, 16, 4096, 4096, 128, 0, FP16) == MAIN
     assert f(1, 1, 128, 128, 64, 0, FP32) == MAIN    # single head fp32
     assert f(96, 1, 512, 512, 128, 0, FP32) == MAIN
     assert f(4, 16, 4096, 4096, 128, 0, BF16) == MAIN
@@ -203,6 +206,7 @@ def test_bwd_invalid(hip_lib):
 
 def test_bwd_unsupported(hip_lib):
     assert bval(hip_lib, dtype=FP32) == UNSUPPORTED
+    assert bval(hip_lib, dtype=FP16) == UNSUPPORTED
     for D in (16, 8, 48, 256):
         assert bval(hip_lib, D=D) == UNSUPPORTED, D
     assert bval(hip_lib, M=1 << 31, N=10) == UNSUPPORTED   # M*D past 32 bits

@@ -112,6 +112,9 @@ def test_checker_on_gpu_tensors(hip_lib):
     qf.requires_grad_(True)
     assert not d.sdpa_checker(qf, kf, vf)[0]               # no fp32 backward
     q16 = qf.detach().half()
-    assert not d.sdpa_checker(q16, q16, q16)[0]            # fp16 inputs
+    assert d.sdpa_checker(q16, q16, q16)[0]                # fp16 forward
+    q16.requires_grad_(True)
+    ok, why = d.sdpa_checker(q16, q16.detach(), q16.detach())
+    assert not ok and "backward" in why                   # no fp16 backward
     ok, why = d.sdpa_checker(q.detach(), k, v, attn_mask=torch.ones(8, 8, device="cuda:0"))
     assert not ok
