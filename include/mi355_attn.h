@@ -48,7 +48,7 @@ extern "C" {
 /* Element type of q, k, v and o. fp16: the Blackwell example's main
  * function describes its test as float16 (its calls pass bf16), and the
  * Thunder page's native-kernel section proposes 16-bit floats. The forward
- * accepts all three types, the backward bf16 only. */
+ * accepts all three types, the backward bf16 and fp16. */
 #define MI355_ATTN_FP32 0
 #define MI355_ATTN_BF16 1
 #define MI355_ATTN_FP16 2
@@ -163,7 +163,8 @@ int attn_fwd_select_path(int64_t B, int64_t H, int64_t M, int64_t N,
  *                while B*H*M > 0; D < 1; non-finite scale; is_causal not 0/1;
  *                bad dtype; dq, dk, dv or delta overlapping an input or each
  *                other (inputs may alias).
- *   UNSUPPORTED  dtype MI355_ATTN_FP32; D not in {32, 64, 128}; a size whose
+ *   UNSUPPORTED  dtype MI355_ATTN_FP32 (bf16 and fp16 are supported); D not
+ *                in {32, 64, 128}; a size whose
  *                element count or launch grid does not fit the kernels'
  *                index types.
  *   MISALIGNED   q, k, v, o, dout, dq, dk or dv not 16-byte aligned, or lse

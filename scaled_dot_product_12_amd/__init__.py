@@ -178,7 +178,7 @@ def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
     shape and dtype. Gradients have the inputs' dtype. ``out=(dq, dk, dv)``
     writes into preallocated tensors; ``delta`` is an optional fp32 [B, H, M]
     workspace (allocated here if None) that receives rowsum(O * dO). bf16
-    only, D in {32, 64, 128}. Asynchronous on torch's current stream.
+    or fp16, D in {32, 64, 128}. Asynchronous on torch's current stream.
     """
     import torch
     B, H, M, N, D = _check(q, k, v)

@@ -95,7 +95,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o,
   if (!k || !v || !dk || !dv) return MI355_ATTN_ERR_INVALID_ARG;
   if (q_rows > 0 && (!q || !o || !lse || !dout || !dq || !delta))
     return MI355_ATTN_ERR_INVALID_ARG;
-  if (dtype != MI355_ATTN_BF16 || !bwd_supported_d(D)) return MI355_ATTN_ERR_UNSUPPORTED;
+  if (dtype == MI355_ATTN_FP32 || !bwd_supported_d(D)) return MI355_ATTN_ERR_UNSUPPORTED;
 
   const int64_t es = 2;
   int64_t md, nd, q_elems, kv_elems, q_bytes, kv_bytes, row_bytes;
@@ -235,7 +235,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.scale = scale;
   a.causal = is_causal != 0;
   a.stream = (hipStream_t)stream;
-  return mi355::launch_bwd_bf16(a) == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
+  const hipError_t err =
+      dtype == MI355_ATTN_FP16 ? mi355::launch_bwd_f16(a) : mi355::launch_bwd_bf16(a);
+  return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 
 const char* attn_status_string(int status) {

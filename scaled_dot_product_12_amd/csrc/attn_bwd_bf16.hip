@@ -1,4 +1,5 @@
-// attn_bwd_bf16.hip -- FlashAttention-2 backward for bf16 inputs on gfx950.
+// attn_bwd_bf16.hip -- FlashAttention-2 backward for 16-bit (bf16, fp16)
+// inputs on gfx950.
 //
 // The gradient of O = softmax(scale Q K^T [+ causal mask]) V for an upstream
 // dO, in the tiled form of "Blackwell Attention Example" (backward kernel
@@ -7,8 +8,8 @@
 // is delta_i = rowsum(O_i * dO_i) (its preprocess kernel), and
 //     dV += P^T dO,   dP = dO V^T,   dS = P (dP - delta),
 //     dK += dS^T Q (times scale),    dQ += dS K (times scale).
-// P and dS are rounded to bf16 before their products, which accumulate in
-// fp32, as on that page.
+// P and dS are rounded to the input type before their products, which
+// accumulate in fp32, as on that page.
 //
 // gfx950 mapping (not the page's design, which accumulates dQ with atomics
 // from the key-tile loop): two kernels, so that every output element has one
@@ -198,22 +199,21 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned cha
 // buffer loads into LDS) to complete.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // Store 16 accumulator registers of a transposed (d by row) product: lane
-// holds d = 32*b + 8*i4 + 4*g + (0..3) of its row, times `mul`, as bf16.
-template <int D>
+// holds d = 32*b + 8*i4 + 4*g + (0..3) of its row, times `mul`, rounded to
+// the 16-bit input type.
+template <int D, bool F16>
 __device__ __forceinline__ void store_rowT(uint16_t* row, const f32x16_t* acc, int g,
                                            float mul) {
+  using H = Half16<F16>;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = b * 32 + i4 * 8 + g * 4;
       u32x2_t st;
-      st[0] = pack_bf16x2(acc[b][i4 * 4 + 0] * mul, acc[b][i4 * 4 + 1] * mul);
-      st[1] = pack_bf16x2(acc[b][i4 * 4 + 2] * mul, acc[b][i4 * 4 + 3] * mul);
+      st[0] = H::pack(acc[b][i4 * 4 + 0] * mul, acc[b][i4 * 4 + 1] * mul);
+      st[1] = H::pack(acc[b][i4 * 4 + 2] * mul, acc[b][i4 * 4 + 3] * mul);
       *(u32x2_t*)(row + d0) = st;
     }
 }
@@ -221,7 +221,7 @@ __device__ __forceinline__ void store_rowT(uint16_t* row, const f32x16_t* acc, i
 }  // namespace
 
 // ---------------------------------------------------------------- dQ kernel
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
@@ -229,6 +229,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
     uint16_t* __restrict__ dq, float* __restrict__ delta, int M, int N, int tiles_m,
     int heads, float c, float scale) {
   using T = Tile<D>;
+  using H = Half16<F16>;
   constexpr int NT = bwd_waves(D) * 64, BM = bwd_waves(D) * 32, BN = kTileRows;
   constexpr int QSTEPS = T::QSTEPS, DBLK = T::DBLK;
   // K ring (2), then V ring (2).
@@ -286,8 +287,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
       const u32x4_t gw = __builtin_bit_cast(u32x4_t, gf[t]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        part = fmaf(bf16_lo(ow[e]), bf16_lo(gw[e]), part);
-        part = fmaf(bf16_hi(ow[e]), bf16_hi(gw[e]), part);
+        part = fmaf(H::lo(ow[e]), H::lo(gw[e]), part);
+        part = fmaf(H::hi(ow[e]), H::hi(gw[e]), part);
       }
     }
     dl = half_pair_sum(part);
@@ -335,8 +336,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
         if (i + PF < NA) fr[(i + PF) % (PF + 1)] = rd(i + PF);
         const int kb = (i >> 1) & 1, t = i >> 2;
         __builtin_amdgcn_sched_barrier(0);
-        if (i & 1) dp[kb] = mfma_32x32x16_bf16(fr[i % (PF + 1)], gf[t], dp[kb]);
-        else s[kb] = mfma_32x32x16_bf16(fr[i % (PF + 1)], qf[t], s[kb]);
+        if (i & 1) dp[kb] = H::mma(fr[i % (PF + 1)], gf[t], dp[kb]);
+        else s[kb] = H::mma(fr[i % (PF + 1)], qf[t], s[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
           const int key = key0 + kb * 32 + g * 16 + i0;
           p0 = masked && (key >= N || (CAUSAL && key > qi)) ? 0.0f : p0;
           p1 = masked && (key + 1 >= N || (CAUSAL && key + 1 > qi)) ? 0.0f : p1;
-          ds[kb][t][e] = pack_bf16x2(p0 * (dp[kb][i0] - dl), p1 * (dp[kb][i0 + 1] - dl));
+          ds[kb][t][e] = H::pack(p0 * (dp[kb][i0] - dl), p1 * (dp[kb][i0 + 1] - dl));
         }
 
     // dQ^T += K^T dS^T over the tile's four 16-key steps (chunk i: d block
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
         if (i + PF < NC) fr[(i + PF) % (PF + 1)] = rd(i + PF);
         const int b = i % DBLK, kt_ = i / DBLK;
         __builtin_amdgcn_sched_barrier(0);
-        acc[b] = mfma_32x32x16_bf16(fr[i % (PF + 1)],
+        acc[b] = H::mma(fr[i % (PF + 1)],
                                     __builtin_bit_cast(bf16x8_t, ds[kt_ >> 1][kt_ & 1]), acc[b]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -386,11 +387,11 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
     __syncthreads();
   }
 
-  if (qi < M) store_rowT<D>(dq + q_off + (size_t)qi * D, acc, g, scale);
+  if (qi < M) store_rowT<D, F16>(dq + q_off + (size_t)qi * D, acc, g, scale);
 }
 
 // ------------------------------------------------------------ dK/dV kernel
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
@@ -398,6 +399,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int M, int N, int tiles_n,
     int heads, float c, float scale) {
   using T = Tile<D>;
+  using H = Half16<F16>;
   constexpr int NT = bwd_waves(D) * 64, BNK = bwd_waves(D) * 32, BQ = kTileRows;
   static_assert(BQ == 64, "one wave loads the 64 per-row statistics of a tile");
   constexpr int QSTEPS = T::QSTEPS, DBLK = T::DBLK;
@@ -532,8 +534,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
         for (int i = 0; i < NA; ++i) {
           if (i + PF < NA) rd(i + PF, fa_[(i + PF) % (PF + 1)], fb_[(i + PF) % (PF + 1)]);
           __builtin_amdgcn_sched_barrier(0);
-          if (i & 1) dp = mfma_32x32x16_bf16(fa_[i % (PF + 1)], fb_[i % (PF + 1)], dp);
-          else s = mfma_32x32x16_bf16(fa_[i % (PF + 1)], fb_[i % (PF + 1)], s);
+          if (i & 1) dp = H::mma(fa_[i % (PF + 1)], fb_[i % (PF + 1)], dp);
+          else s = H::mma(fa_[i % (PF + 1)], fb_[i % (PF + 1)], s);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -555,8 +557,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
               p0 = kj > qq ? 0.0f : p0;
               p1 = kj > qq + 1 ? 0.0f : p1;
             }
-            pb[t][e] = pack_bf16x2(p0, p1);
-            dsb[t][e] = pack_bf16x2(p0 * (dp[i0] - da[2 * e2]), p1 * (dp[i0 + 1] - da[2 * e2 + 1]));
+            pb[t][e] = H::pack(p0, p1);
+            dsb[t][e] = H::pack(p0 * (dp[i0] - da[2 * e2]), p1 * (dp[i0 + 1] - da[2 * e2 + 1]));
           }
         }
       }
@@ -576,9 +578,9 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
           const int t = i / (2 * DBLK), b = (i % (2 * DBLK)) >> 1;
           __builtin_amdgcn_sched_barrier(0);
           if (i & 1)
-            dka[b] = mfma_32x32x16_bf16(fr[i % (PF + 1)], __builtin_bit_cast(bf16x8_t, dsb[t]), dka[b]);
+            dka[b] = H::mma(fr[i % (PF + 1)], __builtin_bit_cast(bf16x8_t, dsb[t]), dka[b]);
           else
-            dva[b] = mfma_32x32x16_bf16(fr[i % (PF + 1)], __builtin_bit_cast(bf16x8_t, pb[t]), dva[b]);
+            dva[b] = H::mma(fr[i % (PF + 1)], __builtin_bit_cast(bf16x8_t, pb[t]), dva[b]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -605,20 +607,20 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
   }
 
   if (kj < N) {
-    store_rowT<D>(dv + kv_off + (size_t)kj * D, dva, g, 1.0f);
-    store_rowT<D>(dk + kv_off + (size_t)kj * D, dka, g, scale);
+    store_rowT<D, F16>(dv + kv_off + (size_t)kj * D, dva, g, 1.0f);
+    store_rowT<D, F16>(dk + kv_off + (size_t)kj * D, dka, g, scale);
   }
 }
 
 // ----------------------------------------------------------------- launch
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 static hipError_t launch_bwd_d(const BwdLaunchArgs& a) {
   const float c = a.scale * kLog2e;
   const int heads = (int)a.BH;
   if (a.M > 0) {
     constexpr int BM = bwd_waves(D) * 32;
     const int tiles_m = (int)((a.M + BM - 1) / BM);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(tiles_m * heads)),
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, F16>), dim3((unsigned)(tiles_m * heads)),
                        dim3(bwd_waves(D) * 64), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
                        a.lse, (const uint16_t*)a.dout, (uint16_t*)a.dq, a.delta, (int)a.M,
@@ -628,7 +630,7 @@ static hipError_t launch_bwd_d(const BwdLaunchArgs& a) {
   }
   constexpr int BNK = bwd_waves(D) * 32;
   const int tiles_n = (int)((a.N + BNK - 1) / BNK);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(tiles_n * heads)),
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, F16>), dim3((unsigned)(tiles_n * heads)),
                      dim3(bwd_waves(D) * 64), 0, a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.delta,
                      (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.M,
@@ -636,14 +638,19 @@ static hipError_t launch_bwd_d(const BwdLaunchArgs& a) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdLaunchArgs& a) {
+template <bool F16>
+static hipError_t launch_bwd_16(const BwdLaunchArgs& a) {
   switch (a.D) {
-    case 32: return a.causal ? launch_bwd_d<32, true>(a) : launch_bwd_d<32, false>(a);
-    case 64: return a.causal ? launch_bwd_d<64, true>(a) : launch_bwd_d<64, false>(a);
-    case 128: return a.causal ? launch_bwd_d<128, true>(a) : launch_bwd_d<128, false>(a);
+    case 32: return a.causal ? launch_bwd_d<32, true, F16>(a) : launch_bwd_d<32, false, F16>(a);
+    case 64: return a.causal ? launch_bwd_d<64, true, F16>(a) : launch_bwd_d<64, false, F16>(a);
+    case 128:
+      return a.causal ? launch_bwd_d<128, true, F16>(a) : launch_bwd_d<128, false, F16>(a);
     default: return hipErrorInvalidValue;
   }
 }
+
+hipError_t launch_bwd_bf16(const BwdLaunchArgs& a) { return launch_bwd_16<false>(a); }
+hipError_t launch_bwd_f16(const BwdLaunchArgs& a) { return launch_bwd_16<true>(a); }
 
 // (the smallest tiles of any head dim: grid-size checks stay conservative)
 int bwd_dq_tile_rows() { return bwd_waves(32) * 32; }

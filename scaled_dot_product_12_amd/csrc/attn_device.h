@@ -74,6 +74,50 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// The two 16-bit input types (bf16, fp16) differ only in the matrix
+// instruction, the rounding of P, dS and outputs, the row-sum dot product and
+// the widening of stored elements. Operands are carried as raw 16-bit lanes.
+template <bool F16>
+struct Half16 {
+  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    if constexpr (F16)
+      return mfma_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c);
+    else
+      return mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                c);
+  }
+  __device__ static f32x16_t mma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return mma(__builtin_bit_cast(u32x4_t, a), __builtin_bit_cast(u32x4_t, b), c);
+  }
+  // Round (p0, p1) to the input type, add the rounded pair to rs, return it packed.
+  __device__ static uint32_t round_sum(float p0, float p1, float& rs) {
+    const f32x2_t f = {p0, p1};
+    if constexpr (F16) {
+      const f16x2_t h = __builtin_convertvector(f, f16x2_t);
+      const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+      rs = __builtin_amdgcn_fdot2(h, one, rs, false);
+      return __builtin_bit_cast(uint32_t, h);
+    } else {
+      const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+      const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+      rs = __builtin_amdgcn_fdot2_f32_bf16(b, one, rs, false);
+      return __builtin_bit_cast(uint32_t, b);
+    }
+  }
+  __device__ static uint32_t pack(float lo, float hi) {
+    return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+  }
+  // The low / high element of a packed pair, widened to fp32 (exact).
+  __device__ static float lo(uint32_t w) {
+    if constexpr (F16) return (float)__builtin_bit_cast(f16x2_t, w)[0];
+    else return __uint_as_float(w << 16);
+  }
+  __device__ static float hi(uint32_t w) {
+    if constexpr (F16) return (float)__builtin_bit_cast(f16x2_t, w)[1];
+    else return __uint_as_float(w & 0xffff0000u);
+  }
+};
+
 // Work-item and workgroup index from the hardware registers. The kernels are
 // built with -mno-amdgpu-ieee, which the device library's threadIdx/blockIdx
 // accessors are not, so those accessors stay out-of-line calls; the builtins

@@ -1,4 +1,5 @@
-// attn_fwd_bf16.hip -- FlashAttention-2 forward for bf16 inputs on gfx950.
+// attn_fwd_bf16.hip -- FlashAttention-2 forward for 16-bit (bf16, fp16)
+// inputs on gfx950.
 //
 // The algorithm is the tiled online softmax of "Extend Thunder with
 // CUDA-Python" (Python reference section): for a tile of query rows, loop
@@ -117,37 +118,6 @@ struct Bf16Cfg {
   }
   __device__ static constexpr int swz_k(int r) { return (r & 15) & (CPR - 1); }
   __device__ static constexpr int swz_v(int r) { return (4 * (r & 3)) & (CPR - 1); }
-};
-
-// The two 16-bit input types differ only in the matrix instruction, the
-// rounding of P and of O, and the row-sum dot product.
-template <bool F16>
-struct Half16 {
-  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    if constexpr (F16)
-      return mfma_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c);
-    else
-      return mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                c);
-  }
-  // Round (p0, p1) to the input type, add the rounded pair to rs, return it packed.
-  __device__ static uint32_t round_sum(float p0, float p1, float& rs) {
-    const f32x2_t f = {p0, p1};
-    if constexpr (F16) {
-      const f16x2_t h = __builtin_convertvector(f, f16x2_t);
-      const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-      rs = __builtin_amdgcn_fdot2(h, one, rs, false);
-      return __builtin_bit_cast(uint32_t, h);
-    } else {
-      const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
-      const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-      rs = __builtin_amdgcn_fdot2_f32_bf16(b, one, rs, false);
-      return __builtin_bit_cast(uint32_t, b);
-    }
-  }
-  __device__ static uint32_t pack(float lo, float hi) {
-    return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
-  }
 };
 
 template <int D, int WAVES, bool CAUSAL, bool POS_SCALE, bool F16>

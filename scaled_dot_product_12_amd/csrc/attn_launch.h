@@ -50,9 +50,10 @@ struct BwdLaunchArgs {
   hipStream_t stream;
 };
 
-// Backward (bf16, D in {32, 64, 128}): dQ kernel (also writes delta), then
-// the dK/dV kernel, both on a.stream.
+// Backward (bf16 or fp16, D in {32, 64, 128}): dQ kernel (also writes
+// delta), then the dK/dV kernel, both on a.stream.
 hipError_t launch_bwd_bf16(const BwdLaunchArgs& a);
+hipError_t launch_bwd_f16(const BwdLaunchArgs& a);
 // Rows per workgroup of the two backward kernels (grid sizing checks).
 int bwd_dq_tile_rows();
 int bwd_dkdv_tile_rows();

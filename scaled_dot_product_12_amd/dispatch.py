@@ -30,6 +30,7 @@ from . import attn_bwd, attn_fwd
 
 FWD_HEAD_DIMS = (16, 32, 64, 128)
 BWD_HEAD_DIMS = (32, 64, 128)
+BWD_DTYPES = (torch.bfloat16, torch.float16)
 
 
 class _Attention(torch.autograd.Function):
@@ -45,9 +46,9 @@ class _Attention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do, _dlse):
         q, k, v, o, lse = ctx.saved_tensors
-        if q.dtype != torch.bfloat16 or q.shape[-1] not in BWD_HEAD_DIMS:
+        if q.dtype not in BWD_DTYPES or q.shape[-1] not in BWD_HEAD_DIMS:
             raise NotImplementedError(
-                f"attention backward supports bf16 with head dim in {BWD_HEAD_DIMS}; "
+                f"attention backward supports bf16 and fp16 with head dim in {BWD_HEAD_DIMS}; "
                 f"got {q.dtype}, D={q.shape[-1]}")
         dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), is_causal=ctx.is_causal,
                               scale=ctx.scale)
@@ -101,8 +102,8 @@ def sdpa_checker(query, key, value, attn_mask=None, dropout_p: float = 0.0,
         return False, "scale is not finite"
     wants_grad = torch.is_grad_enabled() and any(
         t.requires_grad for t in (query, key, value))
-    if wants_grad and (query.dtype != torch.bfloat16 or D not in BWD_HEAD_DIMS):
-        return False, (f"the backward supports bf16 with head dim in {BWD_HEAD_DIMS} "
+    if wants_grad and (query.dtype not in BWD_DTYPES or D not in BWD_HEAD_DIMS):
+        return False, (f"the backward supports bf16 and fp16 with head dim in {BWD_HEAD_DIMS} "
                        f"(inputs require grad)")
     return True, ""
 

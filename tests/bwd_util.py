@@ -1,10 +1,11 @@
 """Helpers for the backward GPU parity tests: run attn_fwd then attn_bwd on
-the GPU, run the fp64 gradient oracle on the same (exact bf16) inputs, and
-compare every element against a bound derived from the arithmetic.
+the GPU, run the fp64 gradient oracle on the same (exact bf16 / fp16) inputs,
+and compare every element against a bound derived from the arithmetic.
 
-The bound (bf16 unit roundoff u = 2^-8, fp32 u32 = 2^-24, lambda = 8):
+The bound (unit roundoff u of the 16-bit input type: 2^-8 for bf16, 2^-11 for
+fp16; fp32 u32 = 2^-24, lambda = 8):
 each gradient element is a sum over n rows of terms a_i, and the kernels
-round each term's factor once to bf16 (P for dV, dS for dK and dQ) with
+round each term's factor once to the input type (P for dV, dS for dK and dQ) with
 errors that are independent between terms, so by Hoeffding's inequality the
 sum's error stays below lambda * u * sqrt(sum_i abar_i^2) except with
 probability 2 exp(-lambda^2 / 2) ~ 2.5e-14 per element. abar_i is the term's
@@ -13,10 +14,10 @@ magnitude with every source of error in it:
     dK_jd:  scale P_ij (|dP_ij| + |delta_i| + dabs_i) |q_id|
     dQ_id:  scale P_ij (|dP_ij| + |delta_i|) |k_jd|
 where dabs_i = sum_d |O_id dO_id| bounds the error of delta_i taken from the
-bf16-rounded forward output (its own rounding and the forward's error, each
+rounded forward output (its own rounding and the forward's error, each
 at most u * dabs_i). In dQ that error is common to the whole row, so it is
 added coherently: 2 u scale dabs_i sum_j P_ij |k_jd|. fp32 accumulation adds
-lambda * sqrt(n) * u32 * sum_i abar_i, and rounding the result to bf16
+lambda * sqrt(n) * u32 * sum_i abar_i, and rounding the result to the input type
 u * |ref|.
 """
 import numpy as np
@@ -26,6 +27,7 @@ import oracle
 import scaled_dot_product_12_amd as attn
 
 U_BF16 = 2.0 ** -8
+U_F16 = 2.0 ** -11
 U_F32 = 2.0 ** -24
 LAMBDA = 8.0
 
@@ -41,9 +43,10 @@ def gpu_fwd_bwd(q, k, v, g, causal, scale):
     return f(dq), f(dk), f(dv), o, lse
 
 
-def head_bounds(q, k, v, g, scale, causal, refs):
+def head_bounds(q, k, v, g, scale, causal, refs, u=U_BF16):
     """Per-element bounds for one head (2-D fp64 arrays q [M,D], k, v [N,D],
-    g [M,D]); refs = oracle (dq, dk, dv) of that head."""
+    g [M,D]); refs = oracle (dq, dk, dv) of that head; u = unit roundoff of
+    the input type."""
     M, N = q.shape[0], k.shape[0]
     o_ref, l_ref = oracle.attn_fwd(q[None, None], k[None, None], v[None, None],
                                    is_causal=causal, scale=scale)
@@ -62,14 +65,14 @@ def head_bounds(q, k, v, g, scale, causal, refs):
         # element (a, d) = sum_i w[i, a] * x[i, d] with w, x >= 0
         rss = np.sqrt((w * w).T @ (x * x))
         s1 = w.T @ x
-        return (LAMBDA * U_BF16 * rss + LAMBDA * np.sqrt(n) * U_F32 * s1
-                + U_BF16 * np.abs(ref) + coherent)
+        return (LAMBDA * u * rss + LAMBDA * np.sqrt(n) * U_F32 * s1
+                + u * np.abs(ref) + coherent)
 
     b_dv = bound(P, np.abs(g), M, dv_ref)
     wk = sc * P * (np.abs(dP) + np.abs(delta)[:, None] + dabs[:, None])
     b_dk = bound(wk, np.abs(q), M, dk_ref)
     wq = sc * P * (np.abs(dP) + np.abs(delta)[:, None])
-    coh = 2.0 * U_BF16 * sc * dabs[:, None] * (P @ np.abs(k))
+    coh = 2.0 * u * sc * dabs[:, None] * (P @ np.abs(k))
     b_dq = bound(wq.T, np.abs(k), N, dq_ref, coherent=coh)
     return b_dq, b_dk, b_dv
 
@@ -90,7 +93,8 @@ def check_heads(q, k, v, g, causal, scale, heads=None, label=""):
     worst = {}
     for (b, h), ref in zip(heads, refs):
         f64 = lambda t: t[b, h].double().numpy()
-        bounds = head_bounds(f64(q), f64(k), f64(v), f64(g), scale, causal, ref)
+        u = U_F16 if q.dtype == torch.float16 else U_BF16
+        bounds = head_bounds(f64(q), f64(k), f64(v), f64(g), scale, causal, ref, u)
         for name, got, r, bd in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref, bounds):
             err = np.abs(got[b, h] - r)
             # a zero bound (every term zero, e.g. keys no query sees) needs

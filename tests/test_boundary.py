@@ -206,7 +206,7 @@ def test_bwd_invalid(hip_lib):
 
 def test_bwd_unsupported(hip_lib):
     assert bval(hip_lib, dtype=FP32) == UNSUPPORTED
-    assert bval(hip_lib, dtype=FP16) == UNSUPPORTED
+    assert bval(hip_lib, dtype=FP16) == OK
     for D in (16, 8, 48, 256):
         assert bval(hip_lib, D=D) == UNSUPPORTED, D
     assert bval(hip_lib, M=1 << 31, N=10) == UNSUPPORTED   # M*D past 32 bits

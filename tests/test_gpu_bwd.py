@@ -1,4 +1,4 @@
-"""GPU parity of the attention backward (attn_bwd, bf16) against the fp64
+"""GPU parity of the attention backward (attn_bwd, bf16 and fp16) against the fp64
 gradient oracle, every element of the compared heads within the bound derived
 in bwd_util.py. Each case runs the GPU forward first and feeds its O and L to
 the backward, as a training step would."""
@@ -16,9 +16,9 @@ from bwd_util import check_heads
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(B, H, M, N, D, seed):
-    q, k, v = make_qkv(B, H, M, N, D, "bf16", seed)
-    return q, k, v, make_dout(B, H, M, D, "bf16", seed)
+def _inputs(B, H, M, N, D, seed, dtype="bf16"):
+    q, k, v = make_qkv(B, H, M, N, D, dtype, seed)
+    return q, k, v, make_dout(B, H, M, D, dtype, seed)
 
 
 def _scale(D):
@@ -31,6 +31,16 @@ def _scale(D):
 def test_bwd_parity(hip_lib, D, causal, M, N):
     q, k, v, g = _inputs(1, 2, M, N, D, seed=M + N + D)
     check_heads(q, k, v, g, causal, _scale(D), label=f"D{D}")
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("M,N", [(200, 200), (130, 300), (65, 1)])
+def test_bwd_parity_fp16(hip_lib, D, causal, M, N):
+    """fp16 inputs: the same kernels with fp16 operands, P and dS rounded to
+    fp16; the bound takes fp16's unit roundoff (2^-11)."""
+    q, k, v, g = _inputs(1, 2, M, N, D, seed=3 * M + N + D, dtype="fp16")
+    check_heads(q, k, v, g, causal, _scale(D), label=f"fp16-D{D}")
 
 
 @pytest.mark.parametrize("M,N", [(1, 1), (1, 200), (200, 1), (5, 3), (64, 64), (65, 129)])
@@ -101,6 +111,13 @@ def test_bwd_c4_shape_sampled_heads(hip_lib):
     times; two whole heads against the oracle."""
     q, k, v, g = _inputs(4, 16, 4096, 4096, 128, seed=4)
     check_heads(q, k, v, g, False, _scale(128), heads=[(0, 0), (3, 15)], label="c4")
+
+
+def test_bwd_c4_shape_fp16_sampled_head(hip_lib):
+    """fp16 B=4 H=16 M=N=4096 D=128 non-causal; one whole head against the
+    oracle."""
+    q, k, v, g = _inputs(4, 16, 4096, 4096, 128, seed=4, dtype="fp16")
+    check_heads(q, k, v, g, False, _scale(128), heads=[(2, 7)], label="c4h")
 
 
 def test_bwd_c5_shape_sampled_head(hip_lib):
