@@ -15,8 +15,9 @@ to this when one tile spans all keys, and whose causal mask keeps key <= query
 in absolute positions); "Blackwell Attention Example", attention kernel (lse as
 one value per query row, [B, H, M]).
 
-Inputs are widened to fp64 exactly (fp32 and bf16 values are representable),
-so for bf16 the oracle sees the bf16-rounded values the GPU sees.
+Inputs are widened to fp64 exactly (fp32, bf16 and fp16 values are
+representable), so for 16-bit inputs the oracle sees the rounded values the
+GPU sees.
 
 The gradient (``attn_bwd``, ``attn_bwd_heads``; see ``attn_oracle_bwd.c``) is
 the chain rule through softmax attention, dQ, dK, dV for an upstream dO, with
@@ -77,7 +78,7 @@ def host_threads() -> int:
 
 
 def _f64(x) -> np.ndarray:
-    """Exact widening of an fp32 / bf16 / fp64 array (numpy or torch) to fp64."""
+    """Exact widening of an fp32 / bf16 / fp16 / fp64 array (numpy or torch) to fp64."""
     if hasattr(x, "detach"):  # torch tensor, possibly bf16 which numpy lacks
         import torch
         x = x.detach().to(device="cpu", dtype=torch.float64).contiguous().numpy()

@@ -247,6 +247,27 @@ def test_rows_api_matches_full():
             assert np.array_equal(ro[t], o[b, h, i]) and rl[t] == l[b, h, i]
 
 
+def _decode16(t, dtype):
+    """fp64 values of a bf16 / fp16 tensor decoded from its raw bits: bf16 is
+    the top half of an fp32 pattern, fp16 is IEEE binary16 (numpy's float16)."""
+    bits = t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_16bit_inputs_are_widened_exactly(dtype):
+    """The oracle consumes 16-bit inputs exactly: the same result, bit for
+    bit, as for the fp64 values decoded from the raw 16-bit patterns."""
+    q, k, v = make_qkv(2, 2, 37, 41, 32, dtype, seed=33)
+    for causal in (False, True):
+        a = oracle.attn_fwd(q, k, v, is_causal=causal, scale=0.2)
+        b = oracle.attn_fwd(*(_decode16(t, dtype) for t in (q, k, v)), is_causal=causal,
+                            scale=0.2)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_thread_count_does_not_change_result():
     q, k, v = _rand(1, 4, 33, 29, 8, seed=29)
     a = oracle.attn_fwd(q, k, v, is_causal=True, scale=0.3, nthreads=1)
