@@ -21,8 +21,9 @@
 //    K(j+1) Q^T on the matrix cores while the vector ALU turns S(j) into
 //    P(j), then O += V(j)^T P(j)^T, whose MFMAs need almost no vector work,
 //    so the two waves of a SIMD overlap one's exponentials with the other's
-//    products. sched_group_barrier interleaves each half (one MFMA, then a
-//    few VALU and LDS instructions).
+//    products. Each half is written as sched_barrier-fenced chunks of one
+//    MFMA plus a share of the vector work and of the operand reads, so the
+//    compiler can neither cluster the MFMAs nor the exponentials.
 //  * The common tile needs no row max. After the first tile sets the
 //    reference m to its exact row max, a tile is exponentiated against the
 //    current m; every p is >= 0, so a lane's partial row sum bounds each of
@@ -68,17 +69,10 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
 // paths (masking, O rescale) stay off the per-tile instruction stream.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x002;
-constexpr int kSgMfma = 0x008;
-constexpr int kSgVmemRead = 0x020;
-constexpr int kSgDsRead = 0x100;
-constexpr int kSgDsWrite = 0x200;
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data
 // format, no swizzle): loads past num_records return zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
-#define MI355_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 }  // namespace
 
@@ -265,25 +259,6 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
       const u32x4_t fr =
           *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
       s[kb] = H::mma(fr, qf[t], s[kb]);
-    }
-  };
-
-  // O^T += V^T P^T for the tile in V buffer buf: fragment i is O block
-  // b = i % DBLK of key step (kb, t) = ((i / DBLK) >> 1, (i / DBLK) & 1).
-  auto pv = [&](int buf, const u32x4_t (*p)[2]) {
-    const unsigned char* vb_base = smem + C::V_OFF + buf * TILEB;
-    const unsigned char* zero = smem + C::ZERO_OFF;
-    typedef __attribute__((ext_vector_type(8))) short s16x8_t;
-#pragma unroll
-    for (int i = 0; i < NF_PV; ++i) {
-      const int b = i % DBLK, kt = i / DBLK, kb = kt >> 1, t = kt & 1;
-      const int row_off = (kb * 32 + t * 8) * ROWB;
-      const unsigned char* a0 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off;
-      const unsigned char* a1 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off + 4 * ROWB;
-      const s16x4_t lo = lds_read_tr16(a0);
-      const s16x4_t hi = lds_read_tr16(a1);
-      const s16x8_t fr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[b] = H::mma(__builtin_bit_cast(u32x4_t, fr), p[kb][t], acc[b]);
     }
   };
 
