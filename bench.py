@@ -235,6 +235,20 @@ def measure(w, steps, warmup, graph):
     return ms, wall, tflops, gbs, tensors
 
 
+def same_bytes_copy_us(nbytes: int, steps: int = 200) -> float:
+    """Time per call of a plain device copy (torch copy_) that reads and
+    writes nbytes / 2 each, i.e. moves the same total bytes as a kernel with
+    nbytes of algorithmic traffic: the practical floor for a microsecond
+    launch of that size (HIP graph of `steps` calls, like the small
+    workloads)."""
+    import torch
+    n = max(1, nbytes // 8)  # fp32 elements per direction
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms, _ = time_launches(lambda: dst.copy_(src), steps, 3, graph=True)
+    return ms * 1e3
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -281,6 +295,10 @@ def main():
                 "gbs": round(xgbs, 1), "frac_hbm_peak": round(xgbs / PEAK_HBM_GBS, 4),
                 "timing": "HIP graph of %d calls" % steps if small else "%d calls" % steps,
             }
+            if x.axial:
+                cus = same_bytes_copy_us(x.algorithmic_bytes())
+                extra[name]["same_bytes_copy_us"] = round(cus, 3)
+                extra[name]["frac_of_copy_rate"] = round(cus / (xms * 1e3), 4)
 
     if not a.no_extra:
         for name in ("c4", "c5", "p64"):
