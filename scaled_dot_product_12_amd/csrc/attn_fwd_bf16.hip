@@ -43,8 +43,10 @@
 //  * V stays row-major in LDS. The A operand V^T of the second product is
 //    read with ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit
 //    elements across each 16-lane group on the way out of LDS.
-//  * K and V tiles are XOR-swizzled at 16-byte granularity so that the MFMA
-//    operand reads of a half-wave hit distinct LDS banks.
+//  * V tiles are XOR-swizzled at 16-byte granularity and K rows padded by
+//    16 bytes, so that the MFMA operand reads of a half-wave hit distinct
+//    LDS banks; the padding makes every K fragment an immediate offset from
+//    one base address per tile.
 //  * Row sums are taken from the bf16-rounded P with v_dot2_f32_bf16, so l
 //    and the second product see the same probabilities.
 //  * Workgroup ids are renumbered so that the query tiles of one head land on
@@ -91,7 +93,13 @@ struct Bf16Cfg {
   static constexpr int BN = 64;                     // keys per tile
   static constexpr int ROWB = D * 2;                // bytes per key row
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
+  static constexpr int TILEB = BN * ROWB;           // bytes per V tile (and of a K tile's data)
+  // K rows sit 16 bytes apart beyond their length in LDS: consecutive rows
+  // then start 4 banks apart, so the 16 rows a half-wave reads at one column
+  // hit 16 distinct 4-bank groups, and a lane's fragment for d-step t is its
+  // row base plus 32 t -- an immediate offset, no per-step address register.
+  static constexpr int KROWB = ROWB + 16;           // LDS bytes per K row
+  static constexpr int KTILEB = BN * KROWB;         // LDS bytes per K tile
   static constexpr int CHUNKS = TILEB / 16;         // 16-byte chunks per tile
   static constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread
   static constexpr int QSTEPS = D / 16;
@@ -100,17 +108,16 @@ struct Bf16Cfg {
   static constexpr int NF_PV = 4 * DBLK;            // MFMAs of one O update
   static constexpr int KBUF = 3;                    // K ring depth
   static constexpr int VBUF = 2;                    // V ring depth
-  static constexpr int V_OFF = KBUF * TILEB;        // K ring, then V ring
+  static constexpr int V_OFF = KBUF * KTILEB;       // K ring, then V ring
   // 64 zero bytes after the rings, read in place of V^T columns past the
   // head (only D = 16 has any); without them two workgroups fit a CU's LDS.
-  static constexpr int ZERO_OFF = (KBUF + VBUF) * TILEB;
+  static constexpr int ZERO_OFF = V_OFF + VBUF * TILEB;
   static constexpr int LDS_BYTES = ZERO_OFF + (D < 32 ? 64 : 0);
-  // K row r of a tile holds key kperm(r); swizzles act on 16-byte chunks.
+  // K row r of a tile holds key kperm(r); the V swizzle acts on 16-byte chunks.
   __device__ static constexpr int kperm(int r) {
     const int b = r & 31;
     return (r & ~31) + ((b >> 2) & 1) * 16 + (b >> 3) * 4 + (b & 3);
   }
-  __device__ static constexpr int swz_k(int r) { return (r & 15) & (CPR - 1); }
   __device__ static constexpr int swz_v(int r) { return (4 * (r & 3)) & (CPR - 1); }
 };
 
@@ -153,20 +160,22 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
 
   if (D < 32 && tid < 16) ((uint32_t*)(smem + C::ZERO_OFF))[tid] = 0u;
 
-  // ---- staging geometry: thread chunk u is LDS chunk ch = tid + u*NT of a
-  // tile, i.e. row ch / CPR at swizzled position ch % CPR. Chunk u sits
-  // RPU = NT / CPR rows below chunk 0 with the same column, and kperm and
-  // the swizzles act on the low row bits only (a bit permutation of bits
-  // 0-4, and bits 0-3), so every per-chunk offset is chunk 0's plus a
+  // ---- staging geometry: thread chunk u is chunk ch = tid + u*NT of a
+  // tile, i.e. row ch / CPR at (for V swizzled) position ch % CPR. Chunk u
+  // sits RPU = NT / CPR rows below chunk 0 with the same column, and kperm
+  // and the V swizzle act on the low row bits only (a bit permutation of
+  // bits 0-4, and bits 0-3), so every per-chunk offset is chunk 0's plus a
   // compile-time constant: one base register per tensor.
   constexpr int RPU = NT / C::CPR;
   int ch0 = tid;
   if (ch0 >= C::CHUNKS) ch0 = C::CHUNKS - 1;  // surplus threads repeat the last chunk
   const int R0 = ch0 / C::CPR, chp0 = ch0 % C::CPR;
   const int dst0 = R0 * ROWB + chp0 * 16;
-  const int k_src0 = 2 * (C::kperm(R0) * D + (chp0 ^ C::swz_k(R0)) * 8);  // bytes from the tile's first key
+  const int kdst0 = R0 * C::KROWB + chp0 * 16;
+  const int k_src0 = 2 * (C::kperm(R0) * D + chp0 * 8);  // bytes from the tile's first key
   const int v_src0 = 2 * (R0 * D + (chp0 ^ C::swz_v(R0)) * 8);
   auto dst_off = [&](int u) { return u * NT * 16; };
+  auto kdst_off = [&](int u) { return u * RPU * C::KROWB; };
   auto k_src_off = [&](int u) { return 2 * C::kperm(u * RPU) * D; };
   auto v_src_off = [&](int u) { return 2 * u * RPU * D; };
   static_assert(CPT == 1 || RPU >= 16, "per-chunk offsets need the row bits of chunk 0 below RPU");
@@ -195,7 +204,8 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   };
   auto store_k = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) *(u32x4_t*)(smem + buf * TILEB + dst0 + dst_off(u)) = kst[u];
+    for (int u = 0; u < CPT; ++u)
+      *(u32x4_t*)(smem + buf * C::KTILEB + kdst0 + kdst_off(u)) = kst[u];
   };
   auto store_v = [&](int buf) {
 #pragma unroll
@@ -205,8 +215,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
 
   // ---- per-lane operand read offsets (bytes within a tile)
   // K (A operand of S^T): LDS row kb*32 + r32, chunk (2t+g) ^ swz.
-  const int k_rd = r32 * ROWB;
-  const int k_sw = C::swz_k(r32);
+  const int k_rd = r32 * C::KROWB;
   // V^T (A operand of O^T) through ds_read_b64_tr_b16: in 16-lane group G,
   // lane 4*jj + cc supplies row (.. + jj) and d-columns 4*cc .. 4*cc+3 of
   // the group's 16-column slice.
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   // S^T = K Q^T for the 64-key tile in K buffer buf: fragment i is key
   // block kb = i & 1 at d-step t = i >> 1.
   auto qk = [&](int buf, f32x16_t* s) {
-    const unsigned char* kb_base = smem + buf * TILEB + k_rd;
+    const unsigned char* kb_base = smem + buf * C::KTILEB + k_rd;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
     for (int i = 0; i < NF_QK; ++i) {
       const int t = i >> 1, kb = i & 1;
       const u32x4_t fr =
-          *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
+          *(const u32x4_t*)(kb_base + kb * 32 * C::KROWB + (2 * t + g) * 16);
       s[kb] = H::mma(fr, qf[t], s[kb]);
     }
   };
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   typedef __attribute__((ext_vector_type(8))) short s16x8_t;
   auto k_frag = [&](const unsigned char* kb_base, int i) -> u32x4_t {
     const int t = i >> 1, kb = i & 1;
-    return *(const u32x4_t*)(kb_base + kb * 32 * ROWB + (((2 * t + g) ^ k_sw) << 4));
+    return *(const u32x4_t*)(kb_base + kb * 32 * C::KROWB + (2 * t + g) * 16);
   };
   auto v_frag = [&](const unsigned char* vb_base, int i) -> s16x8_t {
     const unsigned char* zero = smem + C::ZERO_OFF;
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   auto region_a = [&](int j, const f32x16_t* sc, f32x16_t* sn, u32x4_t (*p)[2])
                       __attribute__((always_inline)) -> float {
     constexpr int PPC = 16 / NF_QK;  // exponential pairs per chunk
-    const unsigned char* kb_base = smem + ((j + 1) % C::KBUF) * TILEB + k_rd;
+    const unsigned char* kb_base = smem + ((j + 1) % C::KBUF) * C::KTILEB + k_rd;
     const auto rk = tile_rsrc(kh, j + 2);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
