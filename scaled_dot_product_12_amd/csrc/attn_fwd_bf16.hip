@@ -483,6 +483,12 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   // Iteration j keeps S(j) in s_a (j even) or s_b (j odd).
   int j = 0;
   for (; j + 2 < nt; j += 2) {
+    // lgkmcnt(0), free here (LDS is drained: the previous iteration ended in
+    // a barrier, the prologue consumed its reads): it tells the
+    // wait-count pass that no scalar load from before the loop is still in
+    // flight, so the first K fragment wait of the iteration counts only its
+    // own LDS read instead of all of them.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     iter(j, s_a, s_b, true);
     iter(j + 1, s_b, s_a, true);
   }
