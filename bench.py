@@ -10,9 +10,10 @@ bf16, resident in HBM before timing starts; outputs are preallocated.
 Prints ONE JSON line with the metric (TFLOP/s with 4*B*H*M*N*D FLOPs, halved
 when causal), the roofline of the dominant kernel, the CPU oracle's rate on a
 bounded sample of the same workload, and the other workloads (fp32 single
-head, fp32 batch-96 non-causal / causal, the two axial passes, bf16 causal
-8192, the Blackwell example's two bench shapes, and the backward at three
-bf16 shapes, 10*B*H*M*N*D FLOPs) as additional measurements.
+head, fp32 batch-96 non-causal / causal, the two axial passes with a
+same-bytes device copy beside them, bf16 causal 8192, the Blackwell example's
+two bench shapes, the headline shape in fp16, and the backward at three bf16
+shapes and the fp16 one, 10*B*H*M*N*D FLOPs) as additional measurements.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
                        [--no-cpu-baseline] [--workload c4]
@@ -301,7 +302,7 @@ def main():
                 extra[name]["frac_of_copy_rate"] = round(cus / (xms * 1e3), 4)
 
     if not a.no_extra:
-        for name in ("c4", "c5", "p64"):
+        for name in ("c4", "c5", "p64", "c4h"):
             x = WORKLOADS[name]
             steps = max(5, min(30, int(4e12 / bwd_flops(x))))
             print(f"[bench] backward {x.describe()}", file=sys.stderr, flush=True)

@@ -37,7 +37,7 @@ def _gpu(*ts):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_sdpa_dropin_is_the_library_forward(hip_lib, dtype, causal):
     d = _dispatch()
@@ -67,13 +67,14 @@ def test_non_contiguous_views(hip_lib):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_autograd_is_the_library_backward(hip_lib, causal):
+def test_autograd_is_the_library_backward(hip_lib, dtype, causal):
     import oracle
-    from bwd_util import head_bounds
+    from bwd_util import U_BF16, U_F16, head_bounds
     d = _dispatch()
-    q0, k0, v0 = make_qkv(1, 2, 190, 170, 128, "bf16", seed=63)
-    g0 = make_dout(1, 2, 190, 128, "bf16", seed=63)
+    q0, k0, v0 = make_qkv(1, 2, 190, 170, 128, dtype, seed=63)
+    g0 = make_dout(1, 2, 190, 128, dtype, seed=63)
     q, k, v = (t.to("cuda:0").requires_grad_(True) for t in (q0, k0, v0))
     g = g0.to("cuda:0")
     o = d.attention(q, k, v, is_causal=causal)
@@ -92,7 +93,7 @@ def test_autograd_is_the_library_backward(hip_lib, causal):
     for h in range(2):
         f64 = lambda t: t[0, h].double().numpy()
         bounds = head_bounds(f64(q0), f64(k0), f64(v0), f64(g0), scale, causal,
-                             tuple(x[0, h] for x in refs))
+                             tuple(x[0, h] for x in refs), U_F16 if dtype == "fp16" else U_BF16)
         for got, r, bd in zip((q.grad, k.grad, v.grad), refs, bounds):
             err = np.abs(got[0, h].float().cpu().double().numpy() - r[0, h])
             assert (err <= bd).all()
