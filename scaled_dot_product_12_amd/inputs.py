@@ -153,3 +153,32 @@ def workload_inputs(w: Workload):
         f = axial_rows if w.axial == "row" else axial_cols
         return f(qi), f(ki), f(vi)
     return make_qkv(w.B, w.H, w.M, w.N, w.D, w.dtype, w.seed)
+
+
+# The fused axial block: an image tensor x [B, Hh, W, C] and the weights of the
+# row pass and of the column pass, each (ln_w [C], ln_b [C], w_qkv [3C, C],
+# w_out [C, C], b_out [C]). Draw order from one generator: x ~ N(0, 1), then
+# for the row pass and then the column pass: ln_w = 1 + 0.1 N(0, 1),
+# ln_b = 0.1 N(0, 1), and w_qkv, w_out, b_out ~ U(-1/sqrt(C), 1/sqrt(C))
+# (torch's default initialisation of its linear layers; the LayerNorm affine is
+# perturbed from its default of (1, 0) so that both terms matter).
+AXIAL_BLOCK_SEED = 6
+
+
+def make_axial_block(B: int = AXIAL_IMAGES, Hh: int = AXIAL_H, W: int = AXIAL_W,
+                     C: int = AXIAL_HEADS * AXIAL_HD, seed: int = AXIAL_BLOCK_SEED):
+    """(x, row_params, col_params) as fp32 CPU tensors."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn((B, Hh, W, C), dtype=torch.float32, generator=g)
+    bound = 1.0 / math.sqrt(C)
+
+    def uniform(shape):
+        return (torch.rand(shape, dtype=torch.float32, generator=g) * 2.0 - 1.0) * bound
+
+    def pass_params():
+        ln_w = 1.0 + 0.1 * torch.randn((C,), dtype=torch.float32, generator=g)
+        ln_b = 0.1 * torch.randn((C,), dtype=torch.float32, generator=g)
+        return (ln_w, ln_b, uniform((3 * C, C)), uniform((C, C)), uniform((C,)))
+
+    row = pass_params()
+    return x, row, pass_params()
