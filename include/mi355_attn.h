@@ -188,6 +188,57 @@ int attn_bwd_validate(const void *q, const void *k, const void *v,
                       int64_t N, int64_t D, float scale, int is_causal,
                       int dtype);
 
+/* ------------------------------------------------------------------------
+ * Fused axial-attention block (the PopcornBench axial-attention trajectory:
+ * the model's reference forward and its per-pass attention helper).
+ *
+ * x and out are fp32 images [B, Hh, W, C], contiguous. One residual pass over
+ * the sequences of one axis (MI355_AXIAL_ROW: each image row (b, y) is a
+ * sequence of W tokens; MI355_AXIAL_COL: each image column (b, x) is a
+ * sequence of Hh tokens) computes, for every token t of every sequence,
+ *
+ *     u    = LayerNorm(x_t) * ln_w + ln_b        biased variance, + eps
+ *     q,k,v = split(u W_qkv^T)                   [3C] read as (3, heads, C/heads)
+ *     a_h  = softmax_j(q_h . k_h,j / sqrt(C/heads)) v_h,j   per head, no mask
+ *     out_t = x_t + concat_h(a_h) W_out^T + b_out
+ *
+ * with the weights stored as torch's linear layers store them: ln_w, ln_b
+ * and b_out [C]; w_qkv [3C, C]; w_out [C, C] (row = output feature); all
+ * fp32, caller-owned device memory. Supported: C = 64, heads = 4, and a
+ * sequence length (W for rows, Hh for columns) of 1..64; other values return
+ * MI355_ATTN_ERR_UNSUPPORTED. out may be x itself (in place); otherwise it
+ * must not overlap x, and it never may overlap a weight. x, out, w_qkv,
+ * w_out, ln_w and ln_b must be 16-byte aligned, b_out 4-byte aligned
+ * (MI355_ATTN_ERR_MISALIGNED). eps must be finite and >= 0; B, Hh, W >= 0
+ * (B * Hh * W = 0 is a no-op). Asynchronous on `stream`, like attn_fwd.
+ */
+#define MI355_AXIAL_ROW 0
+#define MI355_AXIAL_COL 1
+
+int axial_pass(const float *x, float *out, const float *ln_w, const float *ln_b,
+               const float *w_qkv, const float *w_out, const float *b_out,
+               int64_t B, int64_t Hh, int64_t W, int64_t C, int64_t heads,
+               int axis, float eps, void *stream);
+
+/* axial_pass_validate -- the checks of axial_pass without a launch. */
+int axial_pass_validate(const float *x, const float *out, const float *ln_w,
+                        const float *ln_b, const float *w_qkv, const float *w_out,
+                        const float *b_out, int64_t B, int64_t Hh, int64_t W,
+                        int64_t C, int64_t heads, int axis, float eps);
+
+/* axial_block -- the whole block: the row pass from x into out with the
+ * row_* weights, then the column pass on out, in place, with the col_*
+ * weights (the column pass attends over the row pass's result). Two
+ * launches on `stream`; every argument rule of axial_pass applies to both
+ * weight sets, and both sequence lengths must be 1..64. */
+int axial_block(const float *x, float *out, const float *row_ln_w,
+                const float *row_ln_b, const float *row_w_qkv,
+                const float *row_w_out, const float *row_b_out,
+                const float *col_ln_w, const float *col_ln_b,
+                const float *col_w_qkv, const float *col_w_out,
+                const float *col_b_out, int64_t B, int64_t Hh, int64_t W,
+                int64_t C, int64_t heads, float eps, void *stream);
+
 /* attn_status_string -- a static, NUL-terminated name for a status code
  * ("unknown status" for values outside the list above). */
 const char *attn_status_string(int status);

@@ -9,7 +9,10 @@ current stream -- the interface of the pages' wrappers
 in "Extend Thunder with CUDA-Python"; ``(q, k, v) -> (o, lse)`` in
 "Blackwell Attention Example"). ``attn_bwd`` takes the forward's inputs and
 outputs and the upstream gradient dO and returns (dQ, dK, dV), as the
-backward of that page's autograd function does.
+backward of that page's autograd function does. ``axial_pass`` and
+``axial_block`` run the fused axial-attention block (LayerNorm, QKV
+projection, per-head attention, output projection, residual) of the
+PopcornBench axial-attention trajectory on an fp32 image [B, Hh, W, C].
 
 There is no fallback: if the HIP library is missing, every call raises.
 """
@@ -35,10 +38,12 @@ MI355_ATTN_ERR_HIP = 4
 MI355_ATTN_PATH_AUTO = 0
 MI355_ATTN_PATH_MAIN = 1
 MI355_ATTN_PATH_SMALL = 2
+MI355_AXIAL_ROW = 0
+MI355_AXIAL_COL = 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
            "attn_fwd_select_path", "attn_status_string", "attn_bwd",
-           "attn_bwd_validate")
+           "attn_bwd_validate", "axial_pass", "axial_pass_validate", "axial_block")
 
 _lib = None
 
@@ -68,6 +73,12 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = cint
         L.attn_bwd_validate.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint]
         L.attn_bwd_validate.restype = cint
+        L.axial_pass.argtypes = [vp] * 7 + [i64] * 5 + [cint, ctypes.c_float, vp]
+        L.axial_pass.restype = cint
+        L.axial_pass_validate.argtypes = [vp] * 7 + [i64] * 5 + [cint, ctypes.c_float]
+        L.axial_pass_validate.restype = cint
+        L.axial_block.argtypes = [vp] * 12 + [i64] * 5 + [ctypes.c_float, vp]
+        L.axial_block.restype = cint
         L.attn_status_string.argtypes = [cint]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -214,3 +225,69 @@ def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
     if st != MI355_ATTN_OK:
         raise RuntimeError(f"attn_bwd failed: {attn_status_string(st)} ({st})")
     return dq, dk, dv
+
+
+def axial_pass_validate(x, out, ln_w, ln_b, w_qkv, w_out, b_out, B, Hh, W, C, heads,
+                        axis, eps) -> int:
+    """The C checks of axial_pass on raw pointers (integers); no launch."""
+    return lib().axial_pass_validate(x, out, ln_w, ln_b, w_qkv, w_out, b_out, B, Hh, W, C,
+                                     heads, int(axis), float(eps))
+
+
+def _check_axial(x, params, out):
+    import torch
+    if x.device.type != "cuda" or x.dtype != torch.float32 or x.dim() != 4:
+        raise ValueError("x must be an fp32 GPU tensor [B, Hh, W, C]")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    C = x.shape[3]
+    want = ((C,), (C,), (3 * C, C), (C, C), (C,))
+    if len(params) != 5:
+        raise ValueError("params are (ln_w, ln_b, w_qkv, w_out, b_out)")
+    for t, shp in zip(params, want):
+        if (t.device != x.device or t.dtype != torch.float32 or tuple(t.shape) != shp
+                or not t.is_contiguous()):
+            raise ValueError(f"weights must be contiguous fp32 tensors of shapes {want} "
+                             "on x's device")
+    if out is None:
+        out = torch.empty_like(x)
+    elif (out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous()
+          or out.device != x.device):
+        raise ValueError("out must be a contiguous tensor like x")
+    return out
+
+
+def axial_pass(x, params, axis: int, heads: int = 4, eps: float = 1e-5, out=None):
+    """One residual axial-attention pass of the fp32 image x [B, Hh, W, C].
+
+    ``params`` = (ln_w [C], ln_b [C], w_qkv [3C, C], w_out [C, C], b_out [C]);
+    ``axis`` MI355_AXIAL_ROW (sequences along W) or MI355_AXIAL_COL (along Hh).
+    ``out`` may be x itself. Asynchronous on torch's current stream.
+    """
+    import torch
+    out = _check_axial(x, params, out)
+    B, Hh, W, C = x.shape
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = lib().axial_pass(x.data_ptr(), out.data_ptr(), *(t.data_ptr() for t in params),
+                              B, Hh, W, C, int(heads), int(axis), float(eps), stream)
+    if st != MI355_ATTN_OK:
+        raise RuntimeError(f"axial_pass failed: {attn_status_string(st)} ({st})")
+    return out
+
+
+def axial_block(x, row_params, col_params, heads: int = 4, eps: float = 1e-5, out=None):
+    """The row pass into ``out``, then the column pass on ``out`` in place."""
+    import torch
+    out = _check_axial(x, row_params, out)
+    _check_axial(x, col_params, out)
+    B, Hh, W, C = x.shape
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = lib().axial_block(x.data_ptr(), out.data_ptr(),
+                               *(t.data_ptr() for t in row_params),
+                               *(t.data_ptr() for t in col_params),
+                               B, Hh, W, C, int(heads), float(eps), stream)
+    if st != MI355_ATTN_OK:
+        raise RuntimeError(f"axial_block failed: {attn_status_string(st)} ({st})")
+    return out

@@ -16,7 +16,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
-           "attn_fwd_small.hip", "attn_bwd_bf16.hip"]
+           "attn_fwd_small.hip", "attn_bwd_bf16.hip", "axial_api.cpp",
+           "axial_block.hip"]
 
 
 def hipcc() -> str:

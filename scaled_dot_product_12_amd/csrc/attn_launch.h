@@ -58,4 +58,24 @@ hipError_t launch_bwd_f16(const BwdLaunchArgs& a);
 int bwd_dq_tile_rows();
 int bwd_dkdv_tile_rows();
 
+struct AxialLaunchArgs {
+  const float* x;
+  float* out;  // may equal x
+  const float* ln_w;
+  const float* ln_b;
+  const float* w_qkv;
+  const float* w_out;
+  const float* b_out;
+  int64_t nseq;  // sequences (one workgroup each)
+  int64_t L;     // tokens per sequence, 1..64
+  // sequence s starts at (s / inner) * outer_stride + (s % inner) * inner_stride
+  // floats, and its tokens are tstride floats apart
+  int64_t inner, outer_stride, inner_stride, tstride;
+  float eps;
+  hipStream_t stream;
+};
+
+// One residual axial-attention pass (C = 64 features, 4 heads of 16).
+hipError_t launch_axial_pass(const AxialLaunchArgs& a);
+
 }  // namespace mi355

@@ -19,13 +19,14 @@ OK, INVALID, UNSUPPORTED, MISALIGNED, HIPERR = 0, 1, 2, 3, 4
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:attn|axial)_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
-         "attn_status_string", "attn_bwd", "attn_bwd_validate"])
+         "attn_status_string", "attn_bwd", "attn_bwd_validate", "axial_pass",
+         "axial_pass_validate", "axial_block"])
 
 
 def test_library_exports_every_declared_symbol(hip_lib):
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(hip_lib):
 
 def test_header_constants_match_binding(hip_lib):
     text = open(HEADER).read()
-    for name, val in re.findall(r"#define\s+(MI355_ATTN_\w+)\s+(\d+)", text):
+    for name, val in re.findall(r"#define\s+(MI355_(?:ATTN|AXIAL)_\w+)\s+(\d+)", text):
         assert getattr(hip_lib, name) == int(val), name
 
 
