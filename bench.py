@@ -12,8 +12,9 @@ when causal), the roofline of the dominant kernel, the CPU oracle's rate on a
 bounded sample of the same workload, and the other workloads (fp32 single
 head, fp32 batch-96 non-causal / causal, the two axial passes with a
 same-bytes device copy beside them, bf16 causal 8192, the Blackwell example's
-two bench shapes, the headline shape in fp16, and the backward at three bf16
-shapes and the fp16 one, 10*B*H*M*N*D FLOPs) as additional measurements.
+two bench shapes, the headline shape in fp16, the fused axial-attention block
+and its two passes, and the backward at three bf16 shapes and the fp16 one,
+10*B*H*M*N*D FLOPs) as additional measurements.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
                        [--no-cpu-baseline] [--workload c4]
@@ -66,13 +67,21 @@ def copy_calibration(mib: int):
                       "launches": 5}))
 
 
+# What the 16-bit forward kernel is built from: its source, the device header
+# it includes and its hipcc flags. The counter summaries are tied to this.
+TRAFFIC_KERNEL_SOURCES = ("attn_fwd_bf16.hip", "attn_device.h")
+
+
 def kernel_source_hash() -> str:
     import hashlib
+    from scaled_dot_product_12_amd import build as B
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_dot_product_12_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in TRAFFIC_KERNEL_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    flags = B.COMMON + B.KERNEL_FLAGS + B.SOURCE_FLAGS.get(TRAFFIC_KERNEL_SOURCES[0], [])
+    h.update(" ".join(flags).replace(ROOT, "").encode())
     return h.hexdigest()[:16]
 
 
@@ -250,6 +259,53 @@ def same_bytes_copy_us(nbytes: int, steps: int = 200) -> float:
     return ms * 1e3
 
 
+def measure_axial_block(steps: int = 200):
+    """The fused axial-attention block on the pages' images (4 of 32 x 32
+    tokens, C = 64, 4 heads of 16): each pass alone and the whole block (two
+    launches), HIP graph of `steps` calls. FLOPs per pass: 2*C*3C + 2*C*C per
+    token for the projections plus 4*L*d per token and head for the two
+    attention products; algorithmic bytes per pass: the image read once and
+    written once plus the pass's weights."""
+    import torch
+    import scaled_dot_product_12_amd as attn
+    from scaled_dot_product_12_amd.inputs import make_axial_block
+    x, row, col = make_axial_block()
+    B, Hh, W, C = x.shape
+    heads, d = 4, C // 4
+    dev = torch.device("cuda:0")
+    x = x.to(dev)
+    row = tuple(t.to(dev) for t in row)
+    col = tuple(t.to(dev) for t in col)
+    out = torch.empty_like(x)
+    tokens = B * Hh * W
+    wbytes = 4 * (2 * C + 3 * C * C + C * C + C)
+    pass_bytes = 2 * 4 * tokens * C + wbytes
+    res = {}
+    for name, fn, L in (
+            ("axial_row_pass", lambda: attn.axial_pass(x, row, attn.MI355_AXIAL_ROW, out=out), W),
+            ("axial_col_pass", lambda: attn.axial_pass(x, col, attn.MI355_AXIAL_COL, out=out), Hh),
+            ("axial_block", lambda: attn.axial_block(x, row, col, out=out), None)):
+        ms, _ = time_launches(fn, steps, 3, graph=True)
+        if L is None:
+            flops = sum(tokens * (8 * C * C + 4 * heads * l * d) for l in (W, Hh))
+            nbytes = 2 * pass_bytes
+        else:
+            flops = tokens * (8 * C * C + 4 * heads * L * d)
+            nbytes = pass_bytes
+        tf = flops / (ms * 1e-3) / 1e12
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {
+            "workload": f"fused axial {name[6:].replace('_', ' ')} fp32 B={B} Hh={Hh} W={W} "
+                        f"C={C} heads={heads}",
+            "us_per_call": round(ms * 1e3, 3), "tflops": round(tf, 4),
+            "frac_compute_peak": round(tf / PEAK_FP32_TFLOPS, 4),
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "flops_per_call": flops, "algorithmic_bytes": nbytes,
+            "timing": "HIP graph of %d calls" % steps,
+        }
+    return res
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -300,6 +356,10 @@ def main():
                 cus = same_bytes_copy_us(x.algorithmic_bytes())
                 extra[name]["same_bytes_copy_us"] = round(cus, 3)
                 extra[name]["frac_of_copy_rate"] = round(cus / (xms * 1e3), 4)
+
+    if not a.no_extra:
+        print("[bench] extra fused axial block", file=sys.stderr, flush=True)
+        extra.update(measure_axial_block())
 
     if not a.no_extra:
         for name in ("c4", "c5", "p64", "c4h"):

@@ -5,16 +5,20 @@
 // image columns of the row pass's output).
 //
 // One workgroup (4 waves) per sequence of L <= 64 tokens with C = 64 features
-// and 4 heads of 16. Everything between the token load and the final store
-// stays in LDS and registers:
+// and 4 heads of 16, or, when there are fewer sequences than CUs, two
+// workgroups per sequence that each take half of its query tokens (both
+// project K and V for every token; Q, the attention rows, the output
+// projection and the store are split). Everything between the token load and
+// the final store stays in LDS and registers:
 //  * the tokens are gathered straight from the image tensor with the pass's
 //    strides (the column pass needs no transposed copy);
 //  * LayerNorm runs as the tokens arrive: 16 lanes per token, 4 features
 //    each, mean and variance by 16-lane DPP sums;
 //  * the three products (QKV = LN(x) W_qkv^T, S = Q K^T per head, P V, and
 //    the output projection) run on v_mfma_f32_16x16x4f32 in fp32. Wave w
-//    computes QKV column blocks w, w+4, w+8, attention head w and output
-//    column block w, so every SIMD gets the same share;
+//    computes QKV column blocks w, w+4, w+8 (head w's Q, K and V), attention
+//    head w and output column block w, so every SIMD gets the same share and
+//    the attention reads only what its own wave wrote;
 //  * the projection weights are loaded into registers before the tokens, so
 //    their latency overlaps the token load and the LayerNorm.
 //
@@ -69,15 +73,19 @@ __device__ __forceinline__ float row_pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int LP>
+template <int LP, int QS>
 __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
     const float* __restrict__ x, float* out, const float* __restrict__ ln_w,
     const float* __restrict__ ln_b, const float* __restrict__ w_qkv,
     const float* __restrict__ w_out, const float* __restrict__ b_out, int L, int inner,
     int64_t outer_stride, int64_t inner_stride, int64_t tstride, float eps, float c) {
   constexpr int RB = LP / 16;  // 16-token blocks
+  constexpr int QRB = RB / QS;  // query blocks per workgroup
   __shared__ __attribute__((aligned(16))) float xs[LP * kXStr];  // tokens (residual)
-  __shared__ __attribute__((aligned(16))) float xn[LP * kXStr];  // LN(x), then head outputs
+  __shared__ __attribute__((aligned(16))) float xn[LP * kXStr];  // LN(x)
+  // Head outputs: a buffer of their own, since with no barrier after the
+  // projection other waves may still be reading xn.
+  __shared__ __attribute__((aligned(16))) float ao[LP * kXStr];
   __shared__ __attribute__((aligned(16))) float qkv[LP * kQStr];
 
   const int tid = workitem_id();
@@ -85,7 +93,8 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int g = lane >> 4;
-  const int s = workgroup_id();
+  const int s = workgroup_id() / QS;
+  const int q0 = (workgroup_id() % QS) * QRB;  // first query block
   // x and out may be the same buffer: a workgroup reads all of its tokens
   // before it writes any, and sequences are disjoint.
   const int64_t base = (int64_t)(s / inner) * outer_stride + (int64_t)(s % inner) * inner_stride;
@@ -130,7 +139,8 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
   }
   __syncthreads();
 
-  // QKV = LN(x) W_qkv^T: token block rb, feature block wave + 4 cb.
+  // QKV = LN(x) W_qkv^T: token block rb, feature block wave + 4 cb (Q only
+  // for this workgroup's query blocks).
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     f32x4_t a[4];
@@ -139,6 +149,7 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
     for (int e = 0; e < 4; ++e) a[e] = *(const f32x4_t*)(ap + 4 * e);
 #pragma unroll
     for (int cb = 0; cb < 3; ++cb) {
+      if (cb == 0 && (rb < q0 || rb >= q0 + QRB)) continue;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int st = 0; st < 16; ++st) acc = mfma16(a[st >> 2][st & 3], wq[cb][st >> 2][st & 3], acc);
@@ -147,7 +158,11 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
       for (int r = 0; r < 4; ++r) dp[r * kQStr] = acc[r];
     }
   }
-  __syncthreads();
+  // Attention reads only this wave's own QKV columns: LDS operations of a
+  // wave complete in order, so a wave-scope fence (no workgroup barrier) is
+  // enough to keep the compiler from moving the reads above the writes.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 
   // Attention, head = wave. S^T = K Q^T per (key block, query block): rows
   // are keys 16 kb + 4g + r, columns queries; the step-st contraction takes
@@ -156,7 +171,7 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
   {
     const int qo = wave * kHd, ko = kC + wave * kHd, vo = 2 * kC + wave * kHd;
 #pragma unroll
-    for (int qb = 0; qb < RB; ++qb) {
+    for (int qb = q0; qb < q0 + QRB; ++qb) {
       const f32x4_t qf = *(const f32x4_t*)(qkv + (16 * qb + l16) * kQStr + qo + 4 * g);
       f32x4_t sc[RB];
       float mx = -INFINITY;
@@ -190,16 +205,16 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
       const float inv = 1.0f / sum;
       // o[r] is head feature 4g + r of query 16 qb + l16.
       const f32x4_t ov = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-      *(f32x4_t*)(xn + (16 * qb + l16) * kXStr + qo + 4 * g) = ov;
+      *(f32x4_t*)(ao + (16 * qb + l16) * kXStr + qo + 4 * g) = ov;
     }
   }
   __syncthreads();
 
   // Output projection, bias and residual: token block rb, features 16 wave + l16.
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = q0; rb < q0 + QRB; ++rb) {
     f32x4_t a[4];
-    const float* ap = xn + (16 * rb + l16) * kXStr + 16 * g;
+    const float* ap = ao + (16 * rb + l16) * kXStr + 16 * g;
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] = *(const f32x4_t*)(ap + 4 * e);
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -216,18 +231,29 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
 
 }  // namespace
 
+template <int LP, int QS>
+void launch_lp(const AxialLaunchArgs& a, float c) {
+  hipLaunchKernelGGL((axial_pass_kernel<LP, QS>), dim3((unsigned)(a.nseq * QS)), dim3(kWaves * 64),
+                     0, a.stream, a.x, a.out, a.ln_w, a.ln_b, a.w_qkv, a.w_out, a.b_out, (int)a.L,
+                     (int)a.inner, a.outer_stride, a.inner_stride, a.tstride, a.eps, c);
+}
+
+// Query split: two workgroups per sequence while that still leaves at most
+// one per CU (256 CUs); the K and V projections they both do cost less than
+// the idle CUs would.
+constexpr int64_t kSplitBelow = 256 / 2;
+
 hipError_t launch_axial_pass(const AxialLaunchArgs& a) {
-  const dim3 grid((unsigned)a.nseq), block(kWaves * 64);
   // softmax in base 2: scores scaled by log2(e) / sqrt(head dim)
   const float c = (float)(1.4426950408889634 / 4.0);
-  if (a.L <= 32)
-    hipLaunchKernelGGL(axial_pass_kernel<32>, grid, block, 0, a.stream, a.x, a.out, a.ln_w,
-                       a.ln_b, a.w_qkv, a.w_out, a.b_out, (int)a.L, (int)a.inner,
-                       a.outer_stride, a.inner_stride, a.tstride, a.eps, c);
-  else
-    hipLaunchKernelGGL(axial_pass_kernel<64>, grid, block, 0, a.stream, a.x, a.out, a.ln_w,
-                       a.ln_b, a.w_qkv, a.w_out, a.b_out, (int)a.L, (int)a.inner,
-                       a.outer_stride, a.inner_stride, a.tstride, a.eps, c);
+  const bool split = a.nseq <= kSplitBelow;
+  if (a.L <= 32) {
+    if (split) launch_lp<32, 2>(a, c);
+    else launch_lp<32, 1>(a, c);
+  } else {
+    if (split) launch_lp<64, 2>(a, c);
+    else launch_lp<64, 1>(a, c);
+  }
   return hipGetLastError();
 }
 

@@ -33,13 +33,16 @@ def _err(got, want):
     return float(np.abs(g - want).max())
 
 
-SHAPES = [  # (B, Hh, W): the page's images, then ragged and extreme lengths
+SHAPES = [  # (B, Hh, W): the page's images, then ragged and extreme lengths;
+    # up to 128 sequences per pass split each sequence's queries over two
+    # workgroups, more take one workgroup each (the last two shapes)
     (4, 32, 32),
     (2, 7, 45),
     (1, 64, 1),
     (3, 1, 64),
     (1, 17, 33),
     (5, 64, 64),
+    (9, 30, 31),
 ]
 
 
