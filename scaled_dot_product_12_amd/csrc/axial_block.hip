@@ -19,8 +19,8 @@
 //    computes QKV column blocks w, w+4, w+8 (head w's Q, K and V), attention
 //    head w and output column block w, so every SIMD gets the same share and
 //    the attention reads only what its own wave wrote;
-//  * the projection weights are loaded into registers before the tokens, so
-//    their latency overlaps the token load and the LayerNorm.
+//  * the projection weights are loaded into registers right after the
+//    tokens, so their latency overlaps the LayerNorm.
 //
 // v_mfma_f32_16x16x4f32 operand layout (lane l, l16 = l % 16, g = l / 16):
 // A[i][k] at lane i + 16k, B[k][j] at lane j + 16k, D[i][j] in register i % 4
@@ -99,6 +99,22 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
   // before it writes any, and sequences are disjoint.
   const int64_t base = (int64_t)(s / inner) * outer_stride + (int64_t)(s % inner) * inner_stride;
 
+  // Tokens first (16 threads per token, one 16-byte chunk of 4 features
+  // each), then the weights: loads complete in order, so the LayerNorm can
+  // start while the weights are still arriving. Padding tokens load token
+  // L - 1 (L >= 1) and are replaced by 0: no branch, whose join would wait
+  // for the loads before the weights are even issued.
+  const int ch = (tid & 15) * 4;
+  f32x4_t xv[LP / 16];
+#pragma unroll
+  for (int i = 0; i < LP / 16; ++i) {
+    const int t = (tid >> 4) + 16 * i;
+    xv[i] = *(const f32x4_t*)(x + base + (t < L ? t : L - 1) * tstride + ch);
+  }
+  const f32x4_t gam = *(const f32x4_t*)(ln_w + ch);
+  const f32x4_t bet = *(const f32x4_t*)(ln_b + ch);
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights
+
   // Weights: QKV output features 16 (wave + 4 cb) + l16, output-projection
   // feature 16 wave + l16; input features 16g .. 16g + 15.
   f32x4_t wq[3][4], wo[4];
@@ -115,27 +131,21 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
   }
   const float bias = b_out[16 * wave + l16];
 
-  // Tokens and LayerNorm: 16 threads per token, one 16-byte chunk (4
-  // features) each; the mean and the biased variance are 16-lane sums.
-  // Padding tokens are 0 (normalised to the LayerNorm bias, never stored).
-  {
-    const int ch = (tid & 15) * 4;
-    const f32x4_t gam = *(const f32x4_t*)(ln_w + ch);
-    const f32x4_t bet = *(const f32x4_t*)(ln_b + ch);
+  // LayerNorm: the mean and the biased variance of a token are 16-lane sums.
+  // Padding tokens normalise to the LayerNorm bias and are never stored.
 #pragma unroll
-    for (int i = 0; i < LP / 16; ++i) {
-      const int t = (tid >> 4) + 16 * i;
-      f32x4_t val = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (t < L) val = *(const f32x4_t*)(x + base + t * tstride + ch);
-      *(f32x4_t*)(xs + t * kXStr + ch) = val;
-      const float mean = row16_sum((val[0] + val[1]) + (val[2] + val[3])) * (1.0f / kC);
-      const f32x4_t dv = val - mean;
-      const float var =
-          row16_sum((dv[0] * dv[0] + dv[1] * dv[1]) + (dv[2] * dv[2] + dv[3] * dv[3])) *
-          (1.0f / kC);
-      const float rstd = 1.0f / __builtin_sqrtf(var + eps);
-      *(f32x4_t*)(xn + t * kXStr + ch) = dv * rstd * gam + bet;
-    }
+  for (int i = 0; i < LP / 16; ++i) {
+    const int t = (tid >> 4) + 16 * i;
+    const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t val = t < L ? xv[i] : z;
+    *(f32x4_t*)(xs + t * kXStr + ch) = val;
+    const float mean = row16_sum((val[0] + val[1]) + (val[2] + val[3])) * (1.0f / kC);
+    const f32x4_t dv = val - mean;
+    const float var =
+        row16_sum((dv[0] * dv[0] + dv[1] * dv[1]) + (dv[2] * dv[2] + dv[3] * dv[3])) *
+        (1.0f / kC);
+    const float rstd = 1.0f / __builtin_sqrtf(var + eps);
+    *(f32x4_t*)(xn + t * kXStr + ch) = dv * rstd * gam + bet;
   }
   __syncthreads();
 
