@@ -14,7 +14,11 @@ head, fp32 batch-96 non-causal / causal, the two axial passes with a
 same-bytes device copy beside them, bf16 causal 8192, the Blackwell example's
 two bench shapes, the headline shape in fp16, the fused axial-attention block
 and its two passes, and the backward at three bf16 shapes and the fp16 one,
-10*B*H*M*N*D FLOPs) as additional measurements.
+10*B*H*M*N*D FLOPs) as additional measurements. Every measurement times 7
+windows of its steps: the first is the reported figure, all seven give the
+median and minimum per call ("repeat"). The single-head fp32 problem and the
+axial passes are also timed cold, cycling through more independent buffer
+sets than the Infinity Cache and L2 hold ("cold_us_per_call").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
                        [--no-cpu-baseline] [--workload c4]
@@ -22,6 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
 from __future__ import annotations
 
 import argparse
+import statistics
 import json
 import os
 import re
@@ -102,8 +107,15 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, graph=False, spin_s=1.0):
-    """Average GPU time per call (ms) with HIP events on the launch stream.
+# Timed windows per measurement: the first is the reported figure (exactly
+# the requested steps); all of them give the median and the minimum.
+REPS = 7
+
+
+def time_launches(fn, steps, warmup, graph=False, spin_s=1.0, reps=REPS):
+    """Average GPU time per call (ms) with HIP events on the launch stream,
+    over the first timed window of `steps` calls, the wall time of that
+    window, and {median_us, min_us} per call over `reps` such windows.
     graph=True captures the calls in one HIP graph first (for microsecond
     kernels whose Python launch cost would otherwise leave the GPU idle)."""
     import torch
@@ -134,16 +146,22 @@ def time_launches(fn, steps, warmup, graph=False, spin_s=1.0):
         def run():
             for _ in range(steps):
                 fn()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    run()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / steps, wall
+    per_call, wall = [], None
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        run()
+        end.record(stream)
+        torch.cuda.synchronize()
+        if wall is None:
+            wall = time.perf_counter() - t0
+        per_call.append(start.elapsed_time(end) / steps)
+    stats = {"median_us": round(statistics.median(per_call) * 1e3, 3),
+             "min_us": round(min(per_call) * 1e3, 3), "windows": reps}
+    return per_call[0], wall, stats
 
 
 def gpu_setup(w):
@@ -233,16 +251,16 @@ def measure_bwd(w, steps, warmup):
     def fn():
         attn.attn_bwd(q, k, v, o, lse, g, is_causal=w.causal, scale=w.scale,
                       out=(dq, dk, dv), delta=delta)
-    ms, _ = time_launches(fn, steps, warmup)
-    return ms, bwd_flops(w) / (ms * 1e-3) / 1e12
+    ms, _, st = time_launches(fn, steps, warmup)
+    return ms, bwd_flops(w) / (ms * 1e-3) / 1e12, st
 
 
 def measure(w, steps, warmup, graph):
     fn, tensors = gpu_setup(w)
-    ms, wall = time_launches(fn, steps, warmup, graph=graph)
+    ms, wall, st = time_launches(fn, steps, warmup, graph=graph)
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.algorithmic_bytes() / (ms * 1e-3) / 1e9
-    return ms, wall, tflops, gbs, tensors
+    return ms, wall, tflops, gbs, tensors, st
 
 
 def same_bytes_copy_us(nbytes: int, steps: int = 200) -> float:
@@ -255,8 +273,42 @@ def same_bytes_copy_us(nbytes: int, steps: int = 200) -> float:
     n = max(1, nbytes // 8)  # fp32 elements per direction
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
-    ms, _ = time_launches(lambda: dst.copy_(src), steps, 3, graph=True)
+    ms, _, _ = time_launches(lambda: dst.copy_(src), steps, 3, graph=True)
     return ms * 1e3
+
+
+# Bytes one pass over the cold-timing buffer sets must touch: more than the
+# 256 MB Infinity Cache plus the 8 x 4 MB of L2, so every call finds its
+# inputs evicted.
+COLD_BYTES = 320 * 10**6
+
+
+def measure_cold(w, min_calls: int = 200):
+    """Per-call time with cold caches: the calls cycle through independent
+    input/output buffer sets (copies of the workload's tensors) whose total
+    size exceeds the caches, inside one HIP graph. Returns (us, sets)."""
+    import torch
+    import scaled_dot_product_12_amd as attn
+    from scaled_dot_product_12_amd.inputs import workload_inputs
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    nsets = max(2, -(-COLD_BYTES // w.algorithmic_bytes()))
+    sets = []
+    for _ in range(nsets):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        sets.append((q.clone(), k.clone(), v.clone(), o, lse))
+    state = {"i": 0}
+
+    def fn():
+        sq, sk, sv, so, sl = sets[state["i"] % nsets]
+        state["i"] += 1
+        attn.attn_fwd(sq, sk, sv, is_causal=w.causal, scale=w.scale, out=(so, sl))
+    calls = nsets * max(1, -(-min_calls // nsets))
+    ms, _, st = time_launches(fn, calls, 3, graph=True, spin_s=0.2, reps=3)
+    del sets
+    torch.cuda.empty_cache()
+    return ms * 1e3, nsets, st
 
 
 def measure_axial_block(steps: int = 200):
@@ -285,7 +337,7 @@ def measure_axial_block(steps: int = 200):
             ("axial_row_pass", lambda: attn.axial_pass(x, row, attn.MI355_AXIAL_ROW, out=out), W),
             ("axial_col_pass", lambda: attn.axial_pass(x, col, attn.MI355_AXIAL_COL, out=out), Hh),
             ("axial_block", lambda: attn.axial_block(x, row, col, out=out), None)):
-        ms, _ = time_launches(fn, steps, 3, graph=True)
+        ms, _, st = time_launches(fn, steps, 3, graph=True)
         if L is None:
             flops = sum(tokens * (8 * C * C + 4 * heads * l * d) for l in (W, Hh))
             nbytes = 2 * pass_bytes
@@ -301,7 +353,7 @@ def measure_axial_block(steps: int = 200):
             "frac_compute_peak": round(tf / PEAK_FP32_TFLOPS, 4),
             "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "flops_per_call": flops, "algorithmic_bytes": nbytes,
-            "timing": "HIP graph of %d calls" % steps,
+            "timing": "HIP graph of %d calls" % steps, "repeat": st,
         }
     return res
 
@@ -325,7 +377,7 @@ def main():
 
     w = WORKLOADS[a.workload]
     print(f"[bench] headline {w.describe()}", file=sys.stderr, flush=True)
-    ms, wall, tflops, gbs, tensors = measure(w, a.steps, a.warmup, graph=False)
+    ms, wall, tflops, gbs, tensors, head_st = measure(w, a.steps, a.warmup, graph=False)
     del tensors
     torch.cuda.empty_cache()
     print(f"[bench] {ms*1e3:.1f} us/step {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -342,7 +394,7 @@ def main():
             small = x.flops < 1e9
             steps = 200 if small else max(5, min(50, int(2e12 / x.flops)))
             print(f"[bench] extra {x.describe()}", file=sys.stderr, flush=True)
-            xms, _, xtf, xgbs, xt = measure(x, steps, 3, graph=small)
+            xms, _, xtf, xgbs, xt, xst = measure(x, steps, 3, graph=small)
             del xt
             torch.cuda.empty_cache()
             xpeak = PEAK_BF16_TFLOPS if x.dtype in ("bf16", "fp16") else PEAK_FP32_TFLOPS
@@ -351,7 +403,15 @@ def main():
                 "tflops": round(xtf, 3), "frac_compute_peak": round(xtf / xpeak, 4),
                 "gbs": round(xgbs, 1), "frac_hbm_peak": round(xgbs / PEAK_HBM_GBS, 4),
                 "timing": "HIP graph of %d calls" % steps if small else "%d calls" % steps,
+                "repeat": xst,
             }
+            if name in ("c1", "c3r", "c3c"):
+                cus, nsets, cst = measure_cold(x)
+                cgbs = x.algorithmic_bytes() / (cus * 1e-6) / 1e9
+                extra[name].update({
+                    "cold_us_per_call": round(cus, 3), "cold_repeat": cst,
+                    "cold_buffer_sets": nsets, "cold_gbs": round(cgbs, 1),
+                    "cold_frac_hbm_peak": round(cgbs / PEAK_HBM_GBS, 4)})
             if x.axial:
                 cus = same_bytes_copy_us(x.algorithmic_bytes())
                 extra[name]["same_bytes_copy_us"] = round(cus, 3)
@@ -366,13 +426,13 @@ def main():
             x = WORKLOADS[name]
             steps = max(5, min(30, int(4e12 / bwd_flops(x))))
             print(f"[bench] backward {x.describe()}", file=sys.stderr, flush=True)
-            bms, btf = measure_bwd(x, steps, 3)
+            bms, btf, bst = measure_bwd(x, steps, 3)
             torch.cuda.empty_cache()
             extra["bwd_" + name] = {
                 "workload": "backward (dQ, dK, dV) " + x.describe(),
                 "us_per_call": round(bms * 1e3, 3), "tflops": round(btf, 3),
                 "flops_per_call": bwd_flops(x), "frac_compute_peak": round(btf / PEAK_BF16_TFLOPS, 4),
-                "timing": "%d calls" % steps,
+                "timing": "%d calls" % steps, "repeat": bst,
             }
 
     cpu = None
@@ -403,6 +463,7 @@ def main():
         "cpu_baseline": cpu,
         "hbm_gbs_algorithmic": round(gbs, 1),
         "wall_s_timed": round(wall, 4),
+        "repeat": head_st,
         "workloads": extra,
     }
     print(json.dumps(line), flush=True)
