@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--axial-only", action="store_true",
+                    help="only time the fused axial block and its passes (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -375,6 +377,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if a.axial_only:
+        print(json.dumps(measure_axial_block(a.steps)), flush=True)
+        return
     w = WORKLOADS[a.workload]
     print(f"[bench] headline {w.describe()}", file=sys.stderr, flush=True)
     ms, wall, tflops, gbs, tensors, head_st = measure(w, a.steps, a.warmup, graph=False)

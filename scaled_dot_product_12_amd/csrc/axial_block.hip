@@ -77,7 +77,8 @@ template <int LP, int QS>
 __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
     const float* __restrict__ x, float* out, const float* __restrict__ ln_w,
     const float* __restrict__ ln_b, const float* __restrict__ w_qkv,
-    const float* __restrict__ w_out, const float* __restrict__ b_out, int L, int inner,
+    const float* __restrict__ w_out, const float* __restrict__ b_out, int L, int same_xcd,
+    int inner,
     int64_t outer_stride, int64_t inner_stride, int64_t tstride, float eps, float c) {
   constexpr int RB = LP / 16;  // 16-token blocks
   constexpr int QRB = RB / QS;  // query blocks per workgroup
@@ -93,8 +94,20 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int g = lane >> 4;
-  const int s = workgroup_id() / QS;
-  const int q0 = (workgroup_id() % QS) * QRB;  // first query block
+  // Workgroups go to the 8 XCDs round-robin. With two workgroups per
+  // sequence and a sequence count divisible by 8 (same_xcd), the two halves
+  // of a sequence are ids 16a + 8h + x, both on XCD x, so the second reads
+  // the tokens through the L2 the first filled; otherwise ids 2s + h.
+  const int wg = workgroup_id();
+  int s, h;
+  if (QS == 2 && same_xcd) {
+    s = ((wg >> 4) << 3) | (wg & 7);
+    h = (wg >> 3) & 1;
+  } else {
+    s = wg / QS;
+    h = wg % QS;
+  }
+  const int q0 = h * QRB;  // first query block
   // x and out may be the same buffer: a workgroup reads all of its tokens
   // before it writes any, and sequences are disjoint.
   const int64_t base = (int64_t)(s / inner) * outer_stride + (int64_t)(s % inner) * inner_stride;
@@ -245,7 +258,7 @@ template <int LP, int QS>
 void launch_lp(const AxialLaunchArgs& a, float c) {
   hipLaunchKernelGGL((axial_pass_kernel<LP, QS>), dim3((unsigned)(a.nseq * QS)), dim3(kWaves * 64),
                      0, a.stream, a.x, a.out, a.ln_w, a.ln_b, a.w_qkv, a.w_out, a.b_out, (int)a.L,
-                     (int)a.inner, a.outer_stride, a.inner_stride, a.tstride, a.eps, c);
+                     (int)(a.nseq % 8 == 0), (int)a.inner, a.outer_stride, a.inner_stride, a.tstride, a.eps, c);
 }
 
 // Query split: two workgroups per sequence while that still leaves at most
