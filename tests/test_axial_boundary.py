@@ -73,3 +73,21 @@ def test_python_wrapper_rejects_before_any_gpu_call(hip_lib):
         hip_lib.axial_pass(x, p, ROW)            # CPU tensor
     with pytest.raises(ValueError):
         hip_lib.axial_block(x.double(), p, p)
+
+
+def test_block_checks_both_passes_before_any_launch(hip_lib):
+    """axial_block validates the row pass and the column pass (its second
+    weight set, and the column length Hh) before it launches anything."""
+    COL_W = [(i + 8) * SZ for i in range(5)]
+
+    def b(x=X, out=OUT, row=(LNW, LNB, WQKV, WOUT, BOUT), col=tuple(COL_W), B=4, Hh=32, W=32,
+          C=64, heads=4, eps=1e-5):
+        return hip_lib.lib().axial_block(x, out, *row, *col, B, Hh, W, C, heads, eps, None)
+
+    assert b(Hh=65) == UNSUPPORTED          # column length
+    assert b(W=65) == UNSUPPORTED           # row length
+    assert b(col=(0,) + tuple(COL_W[1:])) == INVALID
+    assert b(col=tuple(COL_W[:2]) + (COL_W[2] + 4,) + tuple(COL_W[3:])) == MISALIGNED
+    assert b(col=(OUT,) + tuple(COL_W[1:])) == INVALID   # column weights inside out
+    assert b(out=X + 16) == INVALID
+    assert b(B=0, x=0, out=0) == OK          # empty: nothing launched
