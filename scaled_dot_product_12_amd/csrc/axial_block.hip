@@ -162,23 +162,32 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
   }
   __syncthreads();
 
-  // QKV = LN(x) W_qkv^T: token block rb, feature block wave + 4 cb (Q only
-  // for this workgroup's query blocks).
+  // QKV = LN(x) W_qkv^T, feature blocks wave + 4 cb. This workgroup's query
+  // blocks (i < QRB) take Q, K and V, the other token blocks K and V only;
+  // the loop has a fixed shape (only the block index depends on q0), so the
+  // product chains of a block interleave.
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int i = 0; i < RB; ++i) {
+    const bool own = i < QRB;
+    const int rb = own ? q0 + i : (q0 == 0 ? i : i - QRB);
     f32x4_t a[4];
     const float* ap = xn + (16 * rb + l16) * kXStr + 16 * g;
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] = *(const f32x4_t*)(ap + 4 * e);
+    f32x4_t acc[3];
+#pragma unroll
+    for (int cb = 0; cb < 3; ++cb) acc[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb)
+        if (own || cb > 0) acc[cb] = mfma16(a[st >> 2][st & 3], wq[cb][st >> 2][st & 3], acc[cb]);
 #pragma unroll
     for (int cb = 0; cb < 3; ++cb) {
-      if (cb == 0 && (rb < q0 || rb >= q0 + QRB)) continue;
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int st = 0; st < 16; ++st) acc = mfma16(a[st >> 2][st & 3], wq[cb][st >> 2][st & 3], acc);
+      if (!own && cb == 0) continue;
       float* dp = qkv + (16 * rb + 4 * g) * kQStr + 16 * (wave + 4 * cb) + l16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dp[r * kQStr] = acc[r];
+      for (int r = 0; r < 4; ++r) dp[r * kQStr] = acc[cb][r];
     }
   }
   // Attention reads only this wave's own QKV columns: LDS operations of a
