@@ -202,3 +202,27 @@ def attn_bwd_heads(q, k, v, dout, heads: Iterable[Tuple[int, int]],
                               nthreads=nthreads)
         out.append((dq[0, 0], dk[0, 0], dv[0, 0]))
     return out
+
+
+def attn_fwd_dv(q, k, v, is_causal: bool = False, scale: float | None = None):
+    """Attention whose values have their own head dim Dv (q, k [B,H,*,D],
+    v [B,H,N,Dv]), as the Blackwell example's kernel allows: O [B,H,M,Dv] and
+    L [B,H,M] in fp64. The plain definition with numpy products: scores
+    scale * Q K^T (causal: key j <= query i), row max m, e = exp(s - m),
+    O = e V / sum e, L = m + ln(sum e)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("oracle expects [B,H,M,D] / [B,H,N,D] / [B,H,N,Dv] arrays")
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    if k.shape != (B, H, N, D) or v.shape[:3] != (B, H, N):
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if scale is None:
+        scale = default_scale(D)
+    s = scale * (q @ np.swapaxes(k, -1, -2))
+    if is_causal:
+        s = np.where(np.arange(N)[None, :] > np.arange(M)[:, None], -np.inf, s)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return (e @ v) / l, (m + np.log(l))[..., 0]
