@@ -188,6 +188,27 @@ int attn_bwd_validate(const void *q, const void *k, const void *v,
                       int64_t N, int64_t D, float scale, int is_causal,
                       int dtype);
 
+/* attn_fwd_dv -- attn_fwd with a value head dim Dv of its own ("Blackwell
+ * Attention Example", attention kernel: v may be [.., N, Dv]):
+ *
+ *     O[b,h,i,:] = sum_j softmax(s)_j * v[b,h,j,:]      O is [B, H, M, Dv]
+ *
+ * with s and L exactly as attn_fwd. q and k are [B, H, M, D] / [B, H, N, D],
+ * v is [B, H, N, Dv], o is [B, H, M, Dv], lse [B, H, M] fp32; layout,
+ * ownership, execution and errors as attn_fwd. Dv == D is attn_fwd itself
+ * (every dtype). Dv != D: dtype MI355_ATTN_FP32 only, D and Dv each in
+ * {16, 32, 64, 128}; anything else returns MI355_ATTN_ERR_UNSUPPORTED.
+ */
+int attn_fwd_dv(const void *q, const void *k, const void *v, void *o, float *lse,
+                int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, int64_t Dv,
+                float scale, int is_causal, int dtype, void *stream);
+
+/* attn_fwd_dv_validate -- the checks of attn_fwd_dv without a launch. */
+int attn_fwd_dv_validate(const void *q, const void *k, const void *v, void *o,
+                         const float *lse, int64_t B, int64_t H, int64_t M,
+                         int64_t N, int64_t D, int64_t Dv, float scale,
+                         int is_causal, int dtype);
+
 /* ------------------------------------------------------------------------
  * Fused axial-attention block (the PopcornBench axial-attention trajectory:
  * the model's reference forward and its per-pass attention helper).

@@ -43,7 +43,8 @@ MI355_AXIAL_COL = 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
            "attn_fwd_select_path", "attn_status_string", "attn_bwd",
-           "attn_bwd_validate", "axial_pass", "axial_pass_validate", "axial_block")
+           "attn_bwd_validate", "axial_pass", "axial_pass_validate", "axial_block",
+           "attn_fwd_dv", "attn_fwd_dv_validate")
 
 _lib = None
 
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = cint
         L.attn_bwd_validate.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint]
         L.attn_bwd_validate.restype = cint
+        L.attn_fwd_dv.argtypes = [vp] * 5 + [i64] * 6 + [ctypes.c_float, cint, cint, vp]
+        L.attn_fwd_dv.restype = cint
+        L.attn_fwd_dv_validate.argtypes = [vp] * 5 + [i64] * 6 + [ctypes.c_float, cint, cint]
+        L.attn_fwd_dv_validate.restype = cint
         L.axial_pass.argtypes = [vp] * 7 + [i64] * 5 + [cint, ctypes.c_float, vp]
         L.axial_pass.restype = cint
         L.axial_pass_validate.argtypes = [vp] * 7 + [i64] * 5 + [cint, ctypes.c_float]
@@ -135,7 +140,8 @@ def _check(q, k, v):
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
     B, H, M, D = q.shape
-    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or v.shape != k.shape:
+    if (k.shape[0] != B or k.shape[1] != H or k.shape[3] != D
+            or v.shape[:3] != k.shape[:3]):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
                          f"v {tuple(v.shape)}")
     return B, H, M, k.shape[2], D
@@ -144,7 +150,9 @@ def _check(q, k, v):
 def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
              out: Optional[Tuple] = None,
              path: int = MI355_ATTN_PATH_AUTO):
-    """(O, L) = attention forward of GPU tensors q [B,H,M,D], k, v [B,H,N,D].
+    """(O, L) = attention forward of GPU tensors q [B,H,M,D], k [B,H,N,D],
+    v [B,H,N,Dv] (Dv = D, or for fp32 any other of 16, 32, 64, 128: O is then
+    [B,H,M,Dv], through the C attn_fwd_dv).
 
     O has q's dtype; L is fp32 [B,H,M], natural log. ``scale`` defaults to
     1/sqrt(D). ``out=(o, lse)`` writes into preallocated tensors. ``path``
@@ -153,16 +161,20 @@ def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
     """
     import torch
     B, H, M, N, D = _check(q, k, v)
+    Dv = v.shape[3]
     dt = _dtype_code(q)
     if scale is None:
         scale = default_scale(D)
+    if Dv != D and path != MI355_ATTN_PATH_AUTO:
+        raise ValueError("a value head dim other than D takes the default path")
     if out is None:
-        o = torch.empty_like(q)
+        o = q.new_empty((B, H, M, Dv))
         lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-        if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-            raise ValueError("out[0] must be a contiguous tensor like q")
+        if (tuple(o.shape) != (B, H, M, Dv) or o.dtype != q.dtype
+                or not o.is_contiguous()):
+            raise ValueError("out[0] must be a contiguous [B, H, M, Dv] tensor of q's dtype")
         if (tuple(lse.shape) != (B, H, M) or lse.dtype != torch.float32
                 or not lse.is_contiguous()):
             raise ValueError("out[1] must be a contiguous fp32 [B, H, M] tensor")
@@ -170,10 +182,15 @@ def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
             raise ValueError("out tensors must be on q's device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = lib().attn_fwd_path(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                 o.data_ptr(), lse.data_ptr(), B, H, M, N, D,
-                                 float(scale), int(bool(is_causal)), dt,
-                                 int(path), stream)
+        if Dv != D:
+            st = lib().attn_fwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), B, H, M, N, D, Dv, float(scale),
+                                   int(bool(is_causal)), dt, stream)
+        else:
+            st = lib().attn_fwd_path(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     o.data_ptr(), lse.data_ptr(), B, H, M, N, D,
+                                     float(scale), int(bool(is_causal)), dt,
+                                     int(path), stream)
     if st != MI355_ATTN_OK:
         raise RuntimeError(f"attn_fwd failed: {attn_status_string(st)} ({st})")
     return o, lse
@@ -193,6 +210,8 @@ def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
     """
     import torch
     B, H, M, N, D = _check(q, k, v)
+    if v.shape != k.shape:
+        raise ValueError("attn_bwd needs v with the head dim of q and k")
     dt = _dtype_code(q)
     for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
         if (t.shape != shape or t.dtype != q.dtype or not t.is_contiguous()

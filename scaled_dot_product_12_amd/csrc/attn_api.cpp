@@ -179,6 +179,7 @@ int attn_fwd_path(const void* q, const void* k, const void* v, void* o,
   a.M = M;
   a.N = N;
   a.D = D;
+  a.Dv = D;
   a.scale = scale;
   a.causal = is_causal != 0;
   a.stream = (hipStream_t)stream;
@@ -199,6 +200,78 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int is_causal, int dtype, void* stream) {
   return attn_fwd_path(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype,
                        MI355_ATTN_PATH_AUTO, stream);
+}
+
+// Checks of attn_fwd_dv when the value head dim differs from D: v is
+// [B,H,N,Dv] and o [B,H,M,Dv]; fp32 only.
+static int validate_dv(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                       int64_t Dv, float scale, int is_causal, int dtype) {
+  if (B < 0 || H < 0 || M < 0 || D < 1 || Dv < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return MI355_ATTN_ERR_INVALID_ARG;
+  if (is_causal != 0 && is_causal != 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MI355_ATTN_ERR_INVALID_ARG;
+  int64_t BH, rows;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, M, &rows)) return MI355_ATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return MI355_ATTN_OK;
+  if (N < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse) return MI355_ATTN_ERR_INVALID_ARG;
+  if (dtype != MI355_ATTN_FP32 || !supported_d(D) || !supported_d(Dv))
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  int64_t md, nd, nv, mv, q_el, k_el, v_el, o_el;
+  if (!mul_ok(M, D, &md) || !mul_ok(N, D, &nd) || !mul_ok(N, Dv, &nv) || !mul_ok(M, Dv, &mv) ||
+      md > kIntMax || nd > kIntMax || nv > kIntMax || mv > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (!mul_ok(rows, D, &q_el) || !mul_ok(BH, nd, &k_el) || !mul_ok(BH, nv, &v_el) ||
+      !mul_ok(rows, Dv, &o_el) || q_el > INT64_MAX / 4 || k_el > INT64_MAX / 4 ||
+      v_el > INT64_MAX / 4 || o_el > INT64_MAX / 4)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  const int64_t tile = mi355::main_f32_tile_rows();
+  int64_t grid;
+  if (!mul_ok((M + tile - 1) / tile, BH, &grid) || grid > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+    return MI355_ATTN_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3u) return MI355_ATTN_ERR_MISALIGNED;
+  const int64_t qb = 4 * q_el, kb = 4 * k_el, vb = 4 * v_el, ob = 4 * o_el, lb = 4 * rows;
+  if (overlap(o, ob, q, qb) || overlap(o, ob, k, kb) || overlap(o, ob, v, vb) ||
+      overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, vb) ||
+      overlap(lse, lb, o, ob))
+    return MI355_ATTN_ERR_INVALID_ARG;
+  return MI355_ATTN_OK;
+}
+
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t H, int64_t M, int64_t N, int64_t D, int64_t Dv, float scale,
+                int is_causal, int dtype, void* stream) {
+  if (Dv == D)
+    return attn_fwd_path(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype,
+                         MI355_ATTN_PATH_AUTO, stream);
+  const int st = validate_dv(q, k, v, o, lse, B, H, M, N, D, Dv, scale, is_causal, dtype);
+  if (st != MI355_ATTN_OK) return st;
+  if (B * H * M == 0) return MI355_ATTN_OK;
+  mi355::LaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = B * H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.Dv = Dv;
+  a.scale = scale;
+  a.causal = is_causal != 0;
+  a.stream = (hipStream_t)stream;
+  return mi355::launch_main_f32(a) == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
+}
+
+int attn_fwd_dv_validate(const void* q, const void* k, const void* v, void* o, const float* lse,
+                         int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, int64_t Dv,
+                         float scale, int is_causal, int dtype) {
+  if (Dv == D) return validate(q, k, v, o, lse, B, H, M, N, D, scale, is_causal, dtype);
+  return validate_dv(q, k, v, o, lse, B, H, M, N, D, Dv, scale, is_causal, dtype);
 }
 
 int attn_bwd_validate(const void* q, const void* k, const void* v, const void* o,

@@ -33,7 +33,9 @@ namespace mi355 {
 // SIMDs idle or unevenly loaded.
 constexpr int kF32Waves = 4;
 
-template <int D, int KS, bool CAUSAL>
+// D is the query/key head dim, DV the value (and output) head dim; the
+// Blackwell example's kernel lets them differ.
+template <int D, int DV, int KS, bool CAUSAL>
 __global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
@@ -45,12 +47,15 @@ __global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
   constexpr int BN = 32;
   constexpr int HALF = D / 2;          // d values per lane half
   constexpr int KSTR = D + 4;          // floats per K row in LDS
-  constexpr int DP = D < 32 ? 32 : D;  // V columns the O^T blocks read
-  constexpr int VSTR = DP + 2;         // floats per V row (rows 8-byte aligned)
+  constexpr int DP = DV < 32 ? 32 : DV;  // V columns the O^T blocks read
+  constexpr int VSTR = DP + 2;           // floats per V row (rows 8-byte aligned)
   constexpr int DBLK = DP / 32;
-  constexpr int DCH = D / 4;           // 16-byte chunks per row
-  constexpr int CH = BN * DCH;         // chunks per K (or V) tile
-  constexpr int CPT = (KS * CH + NT - 1) / NT;  // chunks per thread per step (KS tiles)
+  constexpr int DCH = D / 4;             // 16-byte chunks per K row
+  constexpr int DCHV = DV / 4;           // 16-byte chunks per V row
+  constexpr int CH = BN * DCH;           // chunks per K tile
+  constexpr int CHV = BN * DCHV;         // chunks per V tile
+  constexpr int CPT = (KS * CH + NT - 1) / NT;    // K chunks per thread per step (KS tiles)
+  constexpr int CPTV = (KS * CHV + NT - 1) / NT;  // V chunks per thread per step
   constexpr int TILE_F = BN * KSTR + BN * VSTR;  // floats per staged K+V tile
   // partial results of parts 1.. : per lane DBLK*16 accumulators, m, l
   constexpr int PART_F = 64 * (DBLK * 16 + 2);
@@ -72,10 +77,10 @@ __global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
   const int bh = tile.bh, tm = tile.tm;
 
   const size_t q_off = (size_t)bh * M * D;
-  const size_t kv_off = (size_t)bh * N * D;
+  const size_t o_off = (size_t)bh * M * DV;
   const float* qh = q + q_off;
-  const float* kh = k + kv_off;
-  const float* vh = v + kv_off;
+  const float* kh = k + (size_t)bh * N * D;
+  const float* vh = v + (size_t)bh * N * DV;
 
   const int q_wg0 = tm * BM;
   const int qw0 = q_wg0 + rb * 32;
@@ -100,16 +105,19 @@ __global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
   }
   const int steps = (nt + KS - 1) / KS;
 
-  if (D < 32) {  // V columns D..31 stay zero
-    for (int idx = tid; idx < KS * BN * (DP - D); idx += NT) {
-      const int pp = idx / (BN * (DP - D)), rem = idx - pp * (BN * (DP - D));
-      const int row = rem / (DP - D);
-      smem[pp * TILE_F + BN * KSTR + row * VSTR + D + (rem - row * (DP - D))] = 0.0f;
+  if (DV < 32) {  // V columns DV..31 stay zero
+    for (int idx = tid; idx < KS * BN * (DP - DV); idx += NT) {
+      const int pp = idx / (BN * (DP - DV)), rem = idx - pp * (BN * (DP - DV));
+      const int row = rem / (DP - DV);
+      smem[pp * TILE_F + BN * KSTR + row * VSTR + DV + (rem - row * (DP - DV))] = 0.0f;
     }
   }
 
   // Step s stages tile s*KS + pp into buffer pp, for every part pp.
-  f32x4_t kreg[CPT], vreg[CPT];
+  // With equal head dims a K chunk and the V chunk at the same position are
+  // loaded and stored together (one index computation for both); otherwise
+  // the two tiles have their own chunk loops.
+  f32x4_t kreg[CPT], vreg[CPTV];
   auto load_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
@@ -122,12 +130,32 @@ __global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
         f32x4_t xk = {0.0f, 0.0f, 0.0f, 0.0f}, xv = xk;
         if (key < min(N, nt * BN)) {
           xk = *(const f32x4_t*)(kh + (size_t)key * D + col);
-          xv = *(const f32x4_t*)(vh + (size_t)key * D + col);
+          if constexpr (D == DV) xv = *(const f32x4_t*)(vh + (size_t)key * DV + col);
         }
         kreg[u] = xk;
-        vreg[u] = xv;
+        if constexpr (D == DV) vreg[u] = xv;
       }
     }
+    if constexpr (D != DV) {
+#pragma unroll
+      for (int u = 0; u < CPTV; ++u) {
+        const int ch = tid + u * NT;
+        if (ch < KS * CHV) {
+          const int pp = ch / CHV, cl = ch - pp * CHV;
+          const int row = cl / DCHV;
+          const int col = (cl - row * DCHV) * 4;
+          const int key = (st * KS + pp) * BN + row;
+          f32x4_t xv = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (key < min(N, nt * BN)) xv = *(const f32x4_t*)(vh + (size_t)key * DV + col);
+          vreg[u] = xv;
+        }
+      }
+    }
+  };
+  auto store_v = [&](float* vb, int row, int col, const f32x4_t& x) {
+    f32x2_t lo = {x[0], x[1]}, hi = {x[2], x[3]};
+    *(f32x2_t*)(vb + row * VSTR + col) = lo;
+    *(f32x2_t*)(vb + row * VSTR + col + 2) = hi;
   };
   auto store_step = [&]() {
 #pragma unroll
@@ -138,11 +166,20 @@ __global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
         const int row = cl / DCH;
         const int col = (cl - row * DCH) * 4;
         float* kb = smem + pp * TILE_F;
-        float* vb = kb + BN * KSTR;
         *(f32x4_t*)(kb + row * KSTR + col) = kreg[u];
-        f32x2_t lo = {vreg[u][0], vreg[u][1]}, hi = {vreg[u][2], vreg[u][3]};
-        *(f32x2_t*)(vb + row * VSTR + col) = lo;
-        *(f32x2_t*)(vb + row * VSTR + col + 2) = hi;
+        if constexpr (D == DV) store_v(kb + BN * KSTR, row, col, vreg[u]);
+      }
+    }
+    if constexpr (D != DV) {
+#pragma unroll
+      for (int u = 0; u < CPTV; ++u) {
+        const int ch = tid + u * NT;
+        if (ch < KS * CHV) {
+          const int pp = ch / CHV, cl = ch - pp * CHV;
+          const int row = cl / DCHV;
+          const int col = (cl - row * DCHV) * 4;
+          store_v(smem + pp * TILE_F + BN * KSTR, row, col, vreg[u]);
+        }
       }
     }
   };
@@ -257,13 +294,13 @@ __global__ __launch_bounds__(kF32Waves * 64) void attn_fwd_f32_kernel(
   const float l_tot = half_pair_sum(l_run);
   if (qi >= M) return;
   const float inv = 1.0f / l_tot;
-  float* orow = o + q_off + (size_t)qi * D;
+  float* orow = o + o_off + (size_t)qi * DV;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = b * 32 + i4 * 8 + g * 4;
-      if (d0 < D) {
+      if (d0 < DV) {
         f32x4_t st = {acc[b][i4 * 4 + 0] * inv, acc[b][i4 * 4 + 1] * inv,
                       acc[b][i4 * 4 + 2] * inv, acc[b][i4 * 4 + 3] * inv};
         *(f32x4_t*)(orow + d0) = st;
@@ -279,38 +316,49 @@ static int f32_key_split(int64_t BH, int64_t M) {
   return blocks >= 2048 ? 1 : (blocks >= 512 ? 2 : 4);
 }
 
-template <int D, int KS, bool CAUSAL>
+template <int D, int DV, int KS, bool CAUSAL>
 static hipError_t launch_f32_dk(const LaunchArgs& a) {
   constexpr int BM = (kF32Waves / KS) * 32;
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const dim3 grid((unsigned)(tiles_m * a.BH));
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, KS, CAUSAL>), grid, dim3(kF32Waves * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, DV, KS, CAUSAL>), grid, dim3(kF32Waves * 64), 0,
                      a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
                      (float*)a.o, a.lse, (int)a.M, (int)a.N, tiles_m, (int)a.BH,
                      a.scale * kLog2e);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, int DV, bool CAUSAL>
 static hipError_t launch_f32_d(const LaunchArgs& a) {
   switch (f32_key_split(a.BH, a.M)) {
-    case 1: return launch_f32_dk<D, 1, CAUSAL>(a);
-    case 2: return launch_f32_dk<D, 2, CAUSAL>(a);
-    default: return launch_f32_dk<D, 4, CAUSAL>(a);
+    case 1: return launch_f32_dk<D, DV, 1, CAUSAL>(a);
+    case 2: return launch_f32_dk<D, DV, 2, CAUSAL>(a);
+    default: return launch_f32_dk<D, DV, 4, CAUSAL>(a);
   }
 }
 
-template <int D>
+template <int D, int DV>
 static hipError_t launch_f32_dispatch(const LaunchArgs& a) {
-  return a.causal ? launch_f32_d<D, true>(a) : launch_f32_d<D, false>(a);
+  return a.causal ? launch_f32_d<D, DV, true>(a) : launch_f32_d<D, DV, false>(a);
+}
+
+template <int D>
+static hipError_t launch_f32_dv(const LaunchArgs& a) {
+  switch (a.Dv) {
+    case 16: return launch_f32_dispatch<D, 16>(a);
+    case 32: return launch_f32_dispatch<D, 32>(a);
+    case 64: return launch_f32_dispatch<D, 64>(a);
+    case 128: return launch_f32_dispatch<D, 128>(a);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_main_f32(const LaunchArgs& a) {
   switch (a.D) {
-    case 16: return launch_f32_dispatch<16>(a);
-    case 32: return launch_f32_dispatch<32>(a);
-    case 64: return launch_f32_dispatch<64>(a);
-    case 128: return launch_f32_dispatch<128>(a);
+    case 16: return launch_f32_dv<16>(a);
+    case 32: return launch_f32_dv<32>(a);
+    case 64: return launch_f32_dv<64>(a);
+    case 128: return launch_f32_dv<128>(a);
     default: return hipErrorInvalidValue;
   }
 }

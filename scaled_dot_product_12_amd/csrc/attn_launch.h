@@ -15,6 +15,7 @@ struct LaunchArgs {
   float* lse;
   int64_t BH;  // B * H
   int64_t M, N, D;
+  int64_t Dv;  // value and output head dim (equals D except on the fp32 main path)
   float scale;
   bool causal;
   hipStream_t stream;

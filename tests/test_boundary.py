@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
          "attn_status_string", "attn_bwd", "attn_bwd_validate", "axial_pass",
-         "axial_pass_validate", "axial_block"])
+         "axial_pass_validate", "axial_block", "attn_fwd_dv", "attn_fwd_dv_validate"])
 
 
 def test_library_exports_every_declared_symbol(hip_lib):
@@ -239,3 +239,28 @@ def test_bwd_python_wrapper_rejects_before_any_gpu_call(hip_lib):
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         hip_lib.attn_bwd(q, q, q, q, torch.zeros(1, 1, 8), q)   # CPU tensors
+
+
+def test_fwd_dv_validation(hip_lib):
+    """attn_fwd_dv: Dv == D is attn_fwd's checks; Dv != D is fp32 only, with v
+    and o sized by Dv."""
+    L = hip_lib.lib()
+    P = [A, A + SZ, A + 2 * SZ, A + 3 * SZ, A + 4 * SZ]
+
+    def dv(*, ptrs=P, B=2, H=3, M=100, N=70, D=64, Dv=128, scale=0.125, causal=0, dtype=FP32):
+        return L.attn_fwd_dv_validate(*ptrs, B, H, M, N, D, Dv, scale, causal, dtype)
+    assert dv() == OK
+    assert dv(D=128, Dv=16) == OK
+    assert dv(Dv=64, dtype=BF16) == OK                 # equal dims: any dtype
+    assert dv(dtype=BF16) == UNSUPPORTED               # unequal dims: fp32 only
+    assert dv(dtype=FP16) == UNSUPPORTED
+    assert dv(Dv=48) == UNSUPPORTED
+    assert dv(Dv=0) == INVALID
+    assert dv(N=0) == INVALID
+    assert dv(ptrs=[P[0], P[1], 0, P[3], P[4]]) == INVALID
+    assert dv(ptrs=[P[0], P[1], P[2] + 8, P[3], P[4]]) == MISALIGNED
+    assert dv(B=0, ptrs=[0] * 5) == OK
+    # o overlapping the end of v: v is B*H*N*Dv*4 bytes
+    vbytes = 2 * 3 * 70 * 128 * 4
+    assert dv(ptrs=[P[0], P[1], P[2], P[2] + vbytes - 16, P[4]]) == INVALID
+    assert dv(ptrs=[P[0], P[1], P[2], P[2] + vbytes, P[4]]) == OK
