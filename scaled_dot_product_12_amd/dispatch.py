@@ -92,16 +92,22 @@ def sdpa_checker(query, key, value, attn_mask=None, dropout_p: float = 0.0,
     if query.dtype not in (torch.float32, torch.bfloat16, torch.float16):
         return False, f"dtype {query.dtype} is not supported (float32, bfloat16 or float16)"
     B, H, M, D = query.shape
-    if key.shape[:2] != (B, H) or key.shape[3] != D or value.shape != key.shape:
-        return False, "key/value shapes do not match the query (same B, H, D; one N)"
+    if key.shape[:2] != (B, H) or key.shape[3] != D or value.shape[:3] != key.shape[:3]:
+        return False, "key/value shapes do not match the query (same B, H; key's D; one N)"
     if D not in FWD_HEAD_DIMS:
         return False, f"head dim {D} is not supported ({FWD_HEAD_DIMS})"
+    Dv = value.shape[3]
+    if Dv != D and (query.dtype != torch.float32 or Dv not in FWD_HEAD_DIMS):
+        return False, (f"a value head dim other than the query's needs float32 inputs and "
+                       f"Dv in {FWD_HEAD_DIMS}")
     if M > 0 and key.shape[2] == 0:
         return False, "no keys"
     if scale is not None and not math.isfinite(float(scale)):
         return False, "scale is not finite"
     wants_grad = torch.is_grad_enabled() and any(
         t.requires_grad for t in (query, key, value))
+    if wants_grad and Dv != D:
+        return False, "the backward needs the value head dim equal to the query's"
     if wants_grad and (query.dtype not in BWD_DTYPES or D not in BWD_HEAD_DIMS):
         return False, (f"the backward supports bf16 and fp16 with head dim in {BWD_HEAD_DIMS} "
                        f"(inputs require grad)")

@@ -118,3 +118,23 @@ def test_checker_on_gpu_tensors(hip_lib):
     assert d.sdpa_checker(q16, q16.detach(), q16.detach())[0]  # fp16 backward too
     ok, why = d.sdpa_checker(q.detach(), k, v, attn_mask=torch.ones(8, 8, device="cuda:0"))
     assert not ok
+
+
+@pytest.mark.gpu
+def test_sdpa_dropin_value_head_dim_of_its_own(hip_lib):
+    """fp32 with Dv != D runs (attn_fwd_dv, same result as the binding); other
+    dtypes and gradient requests are refused with the reason."""
+    d = _dispatch()
+    q, k, _ = _gpu(*make_qkv(2, 3, 90, 120, 64, "fp32", seed=66))
+    (v,) = _gpu(make_qkv(2, 3, 90, 120, 32, "fp32", seed=67)[2])
+    with torch.no_grad():
+        assert d.sdpa_checker(q, k, v, is_causal=True)[0]
+        o = d.scaled_dot_product_attention(q, k, v, is_causal=True)
+        ref, _ = hip_lib.attn_fwd(q, k, v, is_causal=True)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (2, 3, 90, 32) and torch.equal(o, ref)
+    ok, why = d.sdpa_checker(q.bfloat16(), k.bfloat16(), v.bfloat16())
+    assert not ok and "float32" in why
+    q.requires_grad_(True)
+    ok, why = d.sdpa_checker(q, k, v)
+    assert not ok and "backward" in why
