@@ -52,3 +52,23 @@ def test_equal_dims_through_dv_entry_is_attn_fwd():
                                 torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0 and torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 2, 1, 130), (1, 1, 257, 64), (2, 1, 33, 7)])
+@pytest.mark.parametrize("D,Dv", [(64, 16), (16, 64), (128, 32)])
+def test_dv_edge_shapes(shape, D, Dv):
+    B, H, M, N = shape
+    q, k, v = _inputs(B, H, M, N, D, Dv, seed=70 + M + N)
+    for causal in (False, True):
+        o, lse = attn.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=causal, scale=0.3)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attn_fwd_dv(q, k, v, is_causal=causal, scale=float(np.float32(0.3)))
+        assert np.abs(o.cpu().double().numpy() - ro).max() <= 2e-5
+        assert np.abs(lse.cpu().double().numpy() - rl).max() <= 1e-5
+
+
+def test_dv_empty_queries():
+    q, k, v = _inputs(1, 2, 1, 9, 32, 64, seed=77)
+    o, lse = attn.attn_fwd(q[:, :, :0].contiguous().to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (1, 2, 0, 64) and lse.numel() == 0
