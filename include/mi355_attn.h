@@ -1,6 +1,8 @@
 /*
  * mi355_attn.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward
- * (attn_fwd) and its gradient (attn_bwd).
+ * (attn_fwd; attn_fwd_dv for a value head dim of its own), its gradient
+ * (attn_bwd), and the fused axial-attention block built around it
+ * (axial_pass, axial_block).
  *
  * The operation (FlashAttention-2 forward, as stated by "Extend Thunder with
  * CUDA-Python", Python reference section, and "Blackwell Attention Example",
@@ -28,7 +30,7 @@
  * device. The library allocates nothing, keeps no pointer after a call
  * returns, and has no mutable global state.
  *
- * Execution: attn_fwd and attn_bwd enqueue their kernels on `stream` (a
+ * Execution: every entry point enqueues its kernels on `stream` (a
  * hipStream_t; NULL is the null stream) and return without synchronising.
  * Faults inside a kernel surface at the caller's next synchronisation. Calls
  * are reentrant.
