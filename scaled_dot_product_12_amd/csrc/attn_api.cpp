@@ -203,7 +203,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 // Checks of attn_fwd_dv when the value head dim differs from D: v is
-// [B,H,N,Dv] and o [B,H,M,Dv]; fp32 only.
+// [B,H,N,Dv] and o [B,H,M,Dv]; fp32 for D, Dv in {16, 32, 64, 128}, bf16 and
+// fp16 for (D, Dv) = (64, 128) or (128, 64).
+static bool dv_pair_supported(int64_t D, int64_t Dv, int dtype) {
+  if (!supported_d(D) || !supported_d(Dv)) return false;
+  if (dtype == MI355_ATTN_FP32) return true;
+  return (D == 64 && Dv == 128) || (D == 128 && Dv == 64);
+}
+
 static int validate_dv(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
                        int64_t Dv, float scale, int is_causal, int dtype) {
@@ -216,8 +223,7 @@ static int validate_dv(const void* q, const void* k, const void* v, const void* 
   if (rows == 0) return MI355_ATTN_OK;
   if (N < 1) return MI355_ATTN_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !lse) return MI355_ATTN_ERR_INVALID_ARG;
-  if (dtype != MI355_ATTN_FP32 || !supported_d(D) || !supported_d(Dv))
-    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (!dv_pair_supported(D, Dv, dtype)) return MI355_ATTN_ERR_UNSUPPORTED;
   int64_t md, nd, nv, mv, q_el, k_el, v_el, o_el;
   if (!mul_ok(M, D, &md) || !mul_ok(N, D, &nd) || !mul_ok(N, Dv, &nv) || !mul_ok(M, Dv, &mv) ||
       md > kIntMax || nd > kIntMax || nv > kIntMax || mv > kIntMax)
@@ -226,6 +232,7 @@ static int validate_dv(const void* q, const void* k, const void* v, const void* 
       !mul_ok(rows, Dv, &o_el) || q_el > INT64_MAX / 4 || k_el > INT64_MAX / 4 ||
       v_el > INT64_MAX / 4 || o_el > INT64_MAX / 4)
     return MI355_ATTN_ERR_UNSUPPORTED;
+  const int64_t es = dtype == MI355_ATTN_FP32 ? 4 : 2;
   const int64_t tile = mi355::main_f32_tile_rows();
   int64_t grid;
   if (!mul_ok((M + tile - 1) / tile, BH, &grid) || grid > kIntMax)
@@ -233,7 +240,7 @@ static int validate_dv(const void* q, const void* k, const void* v, const void* 
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
     return MI355_ATTN_ERR_MISALIGNED;
   if ((uintptr_t)lse & 3u) return MI355_ATTN_ERR_MISALIGNED;
-  const int64_t qb = 4 * q_el, kb = 4 * k_el, vb = 4 * v_el, ob = 4 * o_el, lb = 4 * rows;
+  const int64_t qb = es * q_el, kb = es * k_el, vb = es * v_el, ob = es * o_el, lb = 4 * rows;
   if (overlap(o, ob, q, qb) || overlap(o, ob, k, kb) || overlap(o, ob, v, vb) ||
       overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, vb) ||
       overlap(lse, lb, o, ob))
@@ -264,7 +271,10 @@ int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse
   a.scale = scale;
   a.causal = is_causal != 0;
   a.stream = (hipStream_t)stream;
-  return mi355::launch_main_f32(a) == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
+  const hipError_t err = dtype == MI355_ATTN_BF16   ? mi355::launch_main_bf16(a)
+                         : dtype == MI355_ATTN_FP16 ? mi355::launch_main_f16(a)
+                                                    : mi355::launch_main_f32(a);
+  return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 
 int attn_fwd_dv_validate(const void* q, const void* k, const void* v, void* o, const float* lse,

@@ -86,14 +86,19 @@ constexpr int kBf16Waves = 8;
 __host__ __device__ constexpr int bf16_waves(int D) { return D <= 64 ? 4 : kBf16Waves; }
 __host__ __device__ constexpr int bf16_blocks_per_cu(int D) { return D <= 64 ? 3 : 1; }
 
-template <int D, int WAVES>
+// D: query/key head dim; DV: value/output head dim (equal unless the caller
+// gives v a head dim of its own).
+template <int D, int DV, int WAVES>
 struct Bf16Cfg {
   static constexpr int NT = WAVES * 64;
   static constexpr int BM = WAVES * 32;
   static constexpr int BN = 64;                     // keys per tile
   static constexpr int ROWB = D * 2;                // bytes per key row
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int TILEB = BN * ROWB;           // bytes per V tile (and of a K tile's data)
+  static constexpr int TILEB = BN * ROWB;           // bytes of a K tile's data
+  static constexpr int VROWB = DV * 2;              // bytes per value row
+  static constexpr int VCPR = DV / 8;               // 16-byte chunks per value row
+  static constexpr int VTILEB = BN * VROWB;         // bytes per V tile
   // K rows sit 16 bytes apart beyond their length in LDS: consecutive rows
   // then start 4 banks apart, so the 16 rows a half-wave reads at one column
   // hit 16 distinct 4-bank groups, and a lane's fragment for d-step t is its
@@ -101,9 +106,11 @@ struct Bf16Cfg {
   static constexpr int KROWB = ROWB + 16;           // LDS bytes per K row
   static constexpr int KTILEB = BN * KROWB;         // LDS bytes per K tile
   static constexpr int CHUNKS = TILEB / 16;         // 16-byte chunks per tile
-  static constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread
+  static constexpr int CPT = (CHUNKS + NT - 1) / NT;  // K chunks per thread
+  static constexpr int VCHUNKS = VTILEB / 16;
+  static constexpr int VCPT = (VCHUNKS + NT - 1) / NT;  // V chunks per thread
   static constexpr int QSTEPS = D / 16;
-  static constexpr int DBLK = D < 32 ? 1 : D / 32;  // 32-row blocks of O^T
+  static constexpr int DBLK = DV < 32 ? 1 : DV / 32;  // 32-row blocks of O^T
   static constexpr int NF_QK = 2 * QSTEPS;          // MFMAs of one S tile
   static constexpr int NF_PV = 4 * DBLK;            // MFMAs of one O update
   static constexpr int KBUF = 3;                    // K ring depth
@@ -111,24 +118,25 @@ struct Bf16Cfg {
   static constexpr int V_OFF = KBUF * KTILEB;       // K ring, then V ring
   // 64 zero bytes after the rings, read in place of V^T columns past the
   // head (only D = 16 has any); without them two workgroups fit a CU's LDS.
-  static constexpr int ZERO_OFF = V_OFF + VBUF * TILEB;
-  static constexpr int LDS_BYTES = ZERO_OFF + (D < 32 ? 64 : 0);
+  static constexpr int ZERO_OFF = V_OFF + VBUF * VTILEB;
+  static constexpr int LDS_BYTES = ZERO_OFF + (DV < 32 ? 64 : 0);
   // K row r of a tile holds key kperm(r); the V swizzle acts on 16-byte chunks.
   __device__ static constexpr int kperm(int r) {
     const int b = r & 31;
     return (r & ~31) + ((b >> 2) & 1) * 16 + (b >> 3) * 4 + (b & 3);
   }
-  __device__ static constexpr int swz_v(int r) { return (4 * (r & 3)) & (CPR - 1); }
+  __device__ static constexpr int swz_v(int r) { return (4 * (r & 3)) & (VCPR - 1); }
 };
 
-template <int D, int WAVES, bool CAUSAL, bool POS_SCALE, bool F16>
-__global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf16_kernel(
+template <int D, int DV, int WAVES, bool CAUSAL, bool POS_SCALE, bool F16>
+__global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D > DV ? D : DV)) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int M, int N, int tiles_m, int heads, float c) {
-  using C = Bf16Cfg<D, WAVES>;
-  constexpr int NT = C::NT, BM = C::BM, BN = C::BN, ROWB = C::ROWB,
-                TILEB = C::TILEB, CPT = C::CPT, QSTEPS = C::QSTEPS, DBLK = C::DBLK,
+  using C = Bf16Cfg<D, DV, WAVES>;
+  constexpr int NT = C::NT, BM = C::BM, BN = C::BN, ROWB = C::ROWB, VROWB = C::VROWB,
+                VTILEB = C::VTILEB, CPT = C::CPT, VCPT = C::VCPT, QSTEPS = C::QSTEPS,
+                DBLK = C::DBLK,
                 NF_QK = C::NF_QK, NF_PV = C::NF_PV;
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
@@ -143,10 +151,10 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   const int bh = tile.bh, tm = tile.tm;
 
   const size_t q_off = (size_t)bh * M * D;
-  const size_t kv_off = (size_t)bh * N * D;
+  const size_t o_off = (size_t)bh * M * DV;
   const uint16_t* qh = q + q_off;
-  const uint16_t* kh = k + kv_off;
-  const uint16_t* vh = v + kv_off;
+  const uint16_t* kh = k + (size_t)bh * N * D;
+  const uint16_t* vh = v + (size_t)bh * N * DV;
 
   const int q_wg0 = tm * BM;
   const int qw0 = q_wg0 + wave * 32;
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   int nt = (N + BN - 1) / BN;
   if (CAUSAL) nt = min(nt, (min(q_wg0 + BM, M) - 1) / BN + 1);
 
-  if (D < 32 && tid < 16) ((uint32_t*)(smem + C::ZERO_OFF))[tid] = 0u;
+  if (DV < 32 && tid < 16) ((uint32_t*)(smem + C::ZERO_OFF))[tid] = 0u;
 
   // ---- staging geometry: thread chunk u is chunk ch = tid + u*NT of a
   // tile, i.e. row ch / CPR at (for V swizzled) position ch % CPR. Chunk u
@@ -170,26 +178,34 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   int ch0 = tid;
   if (ch0 >= C::CHUNKS) ch0 = C::CHUNKS - 1;  // surplus threads repeat the last chunk
   const int R0 = ch0 / C::CPR, chp0 = ch0 % C::CPR;
-  const int dst0 = R0 * ROWB + chp0 * 16;
   const int kdst0 = R0 * C::KROWB + chp0 * 16;
   const int k_src0 = 2 * (C::kperm(R0) * D + chp0 * 8);  // bytes from the tile's first key
-  const int v_src0 = 2 * (R0 * D + (chp0 ^ C::swz_v(R0)) * 8);
-  auto dst_off = [&](int u) { return u * NT * 16; };
   auto kdst_off = [&](int u) { return u * RPU * C::KROWB; };
   auto k_src_off = [&](int u) { return 2 * C::kperm(u * RPU) * D; };
-  auto v_src_off = [&](int u) { return 2 * u * RPU * D; };
   static_assert(CPT == 1 || RPU >= 16, "per-chunk offsets need the row bits of chunk 0 below RPU");
-  u32x4_t kst[CPT], vst[CPT];
+  // The same geometry for the V tile, whose rows have DV elements.
+  constexpr int VRPU = NT / C::VCPR;
+  int vch0 = tid;
+  if (vch0 >= C::VCHUNKS) vch0 = C::VCHUNKS - 1;
+  const int VR0 = vch0 / C::VCPR, vchp0 = vch0 % C::VCPR;
+  const int dst0 = VR0 * VROWB + vchp0 * 16;
+  const int v_src0 = 2 * (VR0 * DV + (vchp0 ^ C::swz_v(VR0)) * 8);
+  auto dst_off = [&](int u) { return u * NT * 16; };
+  auto v_src_off = [&](int u) { return 2 * u * VRPU * DV; };
+  static_assert(VCPT == 1 || VRPU >= 16, "per-chunk offsets need the row bits of chunk 0 below VRPU");
+  u32x4_t kst[CPT], vst[VCPT];
   // Tile loads go through buffer descriptors bounded by the head's last key
   // row: chunks past it read as zeros (finite, and masked or multiplied by
   // p = 0), so the tail needs no per-lane clamp and tiles past the end need
   // no guard. Offsets are per-lane constants; the tile base is scalar.
-  auto tile_rsrc = [&](const uint16_t* head, int j) {
+  auto tile_rsrc_w = [&](const uint16_t* head, int j, int width) {
     const int jc = min(j, nt - 1);
-    const uint32_t bytes = (uint32_t)(N - jc * BN) * (uint32_t)ROWB;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)jc * BN * D), (short)0,
+    const uint32_t bytes = (uint32_t)(N - jc * BN) * (uint32_t)(2 * width);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)jc * BN * width), (short)0,
                                              (int)bytes, kBufferRsrcWord3);
   };
+  auto tile_rsrc = [&](const uint16_t* head, int j) { return tile_rsrc_w(head, j, D); };
+  auto tile_rsrc_v = [&](int j) { return tile_rsrc_w(vh, j, DV); };
   auto load_k = [&](int j) {
     const auto r = tile_rsrc(kh, j);
 #pragma unroll
@@ -197,9 +213,9 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
       kst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, k_src0 + k_src_off(u), 0, 0);
   };
   auto load_v = [&](int j) {
-    const auto r = tile_rsrc(vh, j);
+    const auto r = tile_rsrc_v(j);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u)
+    for (int u = 0; u < VCPT; ++u)
       vst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, v_src0 + v_src_off(u), 0, 0);
   };
   auto store_k = [&](int buf) {
@@ -209,8 +225,8 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   };
   auto store_v = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u)
-      *(u32x4_t*)(smem + C::V_OFF + buf * TILEB + dst0 + dst_off(u)) = vst[u];
+    for (int u = 0; u < VCPT; ++u)
+      *(u32x4_t*)(smem + C::V_OFF + buf * VTILEB + dst0 + dst_off(u)) = vst[u];
   };
 
   // ---- per-lane operand read offsets (bytes within a tile)
@@ -225,9 +241,9 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) {
     const int d0 = b * 32 + nh * 16 + cc * 4;
-    if (d0 < D) {
+    if (d0 < DV) {
       const int chunk = d0 >> 3;
-      v_rd[b] = (gg * 16 + jj) * ROWB + ((chunk ^ C::swz_v(jj)) << 4) + (cc & 1) * 8;
+      v_rd[b] = (gg * 16 + jj) * VROWB + ((chunk ^ C::swz_v(jj)) << 4) + (cc & 1) * 8;
     } else {
       v_rd[b] = -1;  // d beyond the head: read the zero block
     }
@@ -352,9 +368,9 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   auto v_frag = [&](const unsigned char* vb_base, int i) -> s16x8_t {
     const unsigned char* zero = smem + C::ZERO_OFF;
     const int b = i % DBLK, kt = i / DBLK, kb = kt >> 1, t = kt & 1;
-    const int row_off = (kb * 32 + t * 8) * ROWB;
+    const int row_off = (kb * 32 + t * 8) * VROWB;
     const unsigned char* a0 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off;
-    const unsigned char* a1 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off + 4 * ROWB;
+    const unsigned char* a1 = v_rd[b] < 0 ? zero : vb_base + v_rd[b] + row_off + 4 * VROWB;
     const s16x4_t lo = lds_read_tr16(a0);
     const s16x4_t hi = lds_read_tr16(a1);
     return (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -405,21 +421,21 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   // Second half, as NF_PV fenced chunks: the V^T fragment reads VPF chunks
   // ahead, one O MFMA each and, with a next tile, the loads of V(j+1).
   auto region_b = [&](int j, const u32x4_t (*p)[2], bool has_next) __attribute__((always_inline)) {
-    const unsigned char* vb_base = smem + C::V_OFF + (j & 1) * TILEB;
-    const auto rv = tile_rsrc(vh, j + 1);
+    const unsigned char* vb_base = smem + C::V_OFF + (j & 1) * VTILEB;
+    const auto rv = tile_rsrc_v(j + 1);
     s16x8_t fr[VPF + 1];
 #pragma unroll
     for (int i = 0; i < VPF && i < NF_PV; ++i) fr[i] = v_frag(vb_base, i);
 #pragma unroll
     for (int i = 0; i < NF_PV; ++i) {
       if (i + VPF < NF_PV) fr[(i + VPF) % (VPF + 1)] = v_frag(vb_base, i + VPF);
-      if (has_next && i < CPT)
+      if (has_next && i < VCPT)
         vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_src0 + v_src_off(i), 0, 0);
       const int b = i % DBLK, kt = i / DBLK;
       acc[b] = H::mma(__builtin_bit_cast(u32x4_t, fr[i % (VPF + 1)]), p[kt >> 1][kt & 1], acc[b]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (has_next && NF_PV < CPT) load_v(j + 1);  // (never: NF_PV >= CPT for every D)
+    if (has_next && NF_PV < VCPT) load_v(j + 1);  // (never: NF_PV >= VCPT for every DV)
   };
 
   // Row-sum bound that sends a tile to the exact path: a lane's partial sum
@@ -502,13 +518,13 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   const float l_tot = half_pair_sum(l_run);
   if (qi >= M) return;
   const float inv = 1.0f / l_tot;
-  uint16_t* orow = o + q_off + (size_t)qi * D;
+  uint16_t* orow = o + o_off + (size_t)qi * DV;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = b * 32 + i4 * 8 + g * 4;
-      if (d0 < D) {
+      if (d0 < DV) {
         u32x2_t st;
         st[0] = H::pack(acc[b][i4 * 4 + 0] * inv, acc[b][i4 * 4 + 1] * inv);
         st[1] = H::pack(acc[b][i4 * 4 + 2] * inv, acc[b][i4 * 4 + 3] * inv);
@@ -518,34 +534,41 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D)) void attn_fwd_bf
   if (g == 0) lse[(size_t)bh * M + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool POS, bool F16>
+template <int D, int DV, bool CAUSAL, bool POS, bool F16>
 static hipError_t launch_16_d(const LaunchArgs& a) {
-  constexpr int WAVES = bf16_waves(D);
+  constexpr int WAVES = bf16_waves(D > DV ? D : DV);
   constexpr int BM = WAVES * 32;
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const dim3 grid((unsigned)(tiles_m * a.BH));
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, WAVES, CAUSAL, POS, F16>), grid,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, DV, WAVES, CAUSAL, POS, F16>), grid,
                      dim3(WAVES * 64), 0, a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                      a.lse, (int)a.M, (int)a.N, tiles_m, (int)a.BH, a.scale * kLog2e);
   return hipGetLastError();
 }
 
-template <int D, bool F16>
+template <int D, int DV, bool F16>
 static hipError_t launch_16_dispatch(const LaunchArgs& a) {
   const bool pos = a.scale > 0.0f;
   if (a.causal)
-    return pos ? launch_16_d<D, true, true, F16>(a) : launch_16_d<D, true, false, F16>(a);
-  return pos ? launch_16_d<D, false, true, F16>(a) : launch_16_d<D, false, false, F16>(a);
+    return pos ? launch_16_d<D, DV, true, true, F16>(a) : launch_16_d<D, DV, true, false, F16>(a);
+  return pos ? launch_16_d<D, DV, false, true, F16>(a) : launch_16_d<D, DV, false, false, F16>(a);
 }
 
+// Equal head dims in {16, 32, 64, 128}; a value head dim of its own for the
+// pairs (64, 128) and (128, 64).
 template <bool F16>
 static hipError_t launch_main_16(const LaunchArgs& a) {
+  if (a.Dv != a.D) {
+    if (a.D == 64 && a.Dv == 128) return launch_16_dispatch<64, 128, F16>(a);
+    if (a.D == 128 && a.Dv == 64) return launch_16_dispatch<128, 64, F16>(a);
+    return hipErrorInvalidValue;
+  }
   switch (a.D) {
-    case 16: return launch_16_dispatch<16, F16>(a);
-    case 32: return launch_16_dispatch<32, F16>(a);
-    case 64: return launch_16_dispatch<64, F16>(a);
-    case 128: return launch_16_dispatch<128, F16>(a);
+    case 16: return launch_16_dispatch<16, 16, F16>(a);
+    case 32: return launch_16_dispatch<32, 32, F16>(a);
+    case 64: return launch_16_dispatch<64, 64, F16>(a);
+    case 128: return launch_16_dispatch<128, 128, F16>(a);
     default: return hipErrorInvalidValue;
   }
 }

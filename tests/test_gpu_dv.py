@@ -1,6 +1,7 @@
-"""GPU parity of attention with a value head dim of its own (attn_fwd_dv,
-fp32): the HIP path against oracle.attn_fwd_dv on every element, at the fp32
-bounds (|dO| <= 2e-5, |dL| <= 1e-5). The shapes span several key tiles with
+"""GPU parity of attention with a value head dim of its own (attn_fwd_dv):
+the HIP path against oracle.attn_fwd_dv on every element, at the fp32 bounds
+(|dO| <= 2e-5, |dL| <= 1e-5) and, for the 16-bit pairs (64, 128) and
+(128, 64), at the bf16 / fp16 bounds with the oracle on the rounded inputs. The shapes span several key tiles with
 ragged tails and the three key-split settings of the fp32 kernel (problems
 with few, some and many 32-row blocks)."""
 import numpy as np
@@ -72,3 +73,23 @@ def test_dv_empty_queries():
     o, lse = attn.attn_fwd(q[:, :, :0].contiguous().to(DEV), k.to(DEV), v.to(DEV))
     torch.cuda.synchronize()
     assert tuple(o.shape) == (1, 2, 0, 64) and lse.numel() == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("D,Dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 4, 300, 200), (1, 2, 65, 1), (1, 1, 513, 700)])
+def test_dv_16bit_matches_oracle(dtype, D, Dv, causal, shape):
+    from parity_util import TOL
+    B, H, M, N = shape
+    q, k, _ = make_qkv(B, H, M, N, D, dtype, seed=80 + D)
+    _, _, v = make_qkv(B, H, M, N, Dv, dtype, seed=81 + Dv)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    print(f"[dv16] {dtype} shape={shape} D={D} Dv={Dv} causal={causal}", flush=True)
+    o, lse = attn.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (B, H, M, Dv) and o.dtype == q.dtype
+    ro, rl = oracle.attn_fwd_dv(q, k, v, is_causal=causal, scale=scale)
+    to, tl = TOL[dtype]
+    assert np.abs(o.float().cpu().double().numpy() - ro).max() <= to
+    assert np.abs(lse.cpu().double().numpy() - rl).max() <= tl
