@@ -13,8 +13,8 @@ bounded sample of the same workload, and the other workloads (fp32 single
 head, fp32 batch-96 non-causal / causal, the two axial passes with a
 same-bytes device copy beside them, bf16 causal 8192, the Blackwell example's
 two bench shapes, the headline shape in fp16, the fused axial-attention block
-and its two passes, the fp32 batch with a value head dim of its own (Dv = 64
-beside D = 128), and the backward at three bf16 shapes and the fp16 one,
+and its two passes, the fp32 batch and the long bf16 shape with a value head dim
+of its own (Dv = 64 beside D = 128), and the backward at three bf16 shapes and the fp16 one,
 10*B*H*M*N*D FLOPs) as additional measurements. Every measurement times 7
 windows of its steps: the first is the reported figure, all seven give the
 median and minimum per call ("repeat"). The single-head fp32 problem and the
@@ -314,29 +314,39 @@ def measure_cold(w, min_calls: int = 200):
     return ms * 1e3, nsets, st
 
 
-def measure_dv(steps: int = 50):
-    """Attention with a value head dim of its own on the Thunder notebook's
-    batch (fp32, 96 x 512 x 512, D = 128) with Dv = 64: FLOPs
-    2*B*H*M*N*(D + Dv), algorithmic bytes Q, K, V, O and L once."""
+def measure_dv(steps: int = 30):
+    """Attention with a value head dim of its own, Dv = 64 beside D = 128: on
+    the Thunder notebook's fp32 batch (96 x 512 x 512) and on the
+    long-sequence bf16 shape (4 x 16 x 4096 x 4096). FLOPs
+    2*B*H*M*N*(D + Dv); algorithmic bytes Q, K, V, O and L once."""
     import torch
     import scaled_dot_product_12_amd as attn
     from scaled_dot_product_12_amd.inputs import make_qkv
-    B, H, M, N, D, Dv = 96, 1, 512, 512, 128, 64
     dev = torch.device("cuda:0")
-    q, k, _ = (t.to(dev) for t in make_qkv(B, H, M, N, D, "fp32", seed=2))
-    _, _, v = (t.to(dev) for t in make_qkv(B, H, M, N, Dv, "fp32", seed=3))
-    o = torch.empty((B, H, M, Dv), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, H, M), dtype=torch.float32, device=dev)
-    ms, _, st = time_launches(lambda: attn.attn_fwd(q, k, v, out=(o, lse)), steps, 3)
-    flops = 2 * B * H * M * N * (D + Dv)
-    nbytes = 4 * B * H * (M * D + N * D + N * Dv + M * Dv + M)
-    tf = flops / (ms * 1e-3) / 1e12
-    return {"dv_c2": {
-        "workload": f"fp32 B={B} H={H} M={M} N={N} D={D} Dv={Dv} non-causal (value head dim of its own)",
-        "us_per_call": round(ms * 1e3, 3), "tflops": round(tf, 3),
-        "frac_compute_peak": round(tf / PEAK_FP32_TFLOPS, 4),
-        "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "flops_per_call": flops,
-        "timing": "%d calls" % steps, "repeat": st}}
+    res = {}
+    for name, dtype, (B, H, M, N), seeds in (("dv_c2", "fp32", (96, 1, 512, 512), (2, 3)),
+                                            ("dv_c4", "bf16", (4, 16, 4096, 4096), (4, 5))):
+        D, Dv = 128, 64
+        q, k, _ = (t.to(dev) for t in make_qkv(B, H, M, N, D, dtype, seed=seeds[0]))
+        v = make_qkv(B, H, M, N, Dv, dtype, seed=seeds[1])[2].to(dev)
+        o = torch.empty((B, H, M, Dv), dtype=q.dtype, device=dev)
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+        ms, _, st = time_launches(lambda: attn.attn_fwd(q, k, v, out=(o, lse)), steps, 3)
+        es = q.element_size()
+        flops = 2 * B * H * M * N * (D + Dv)
+        nbytes = es * B * H * (M * D + N * D + N * Dv + M * Dv) + 4 * B * H * M
+        tf = flops / (ms * 1e-3) / 1e12
+        peak = PEAK_FP32_TFLOPS if dtype == "fp32" else PEAK_BF16_TFLOPS
+        res[name] = {
+            "workload": f"{dtype} B={B} H={H} M={M} N={N} D={D} Dv={Dv} non-causal "
+                        "(value head dim of its own)",
+            "us_per_call": round(ms * 1e3, 3), "tflops": round(tf, 3),
+            "frac_compute_peak": round(tf / peak, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "flops_per_call": flops,
+            "timing": "%d calls" % steps, "repeat": st}
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return res
 
 
 def measure_axial_block(steps: int = 200):
