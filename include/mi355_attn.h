@@ -198,10 +198,8 @@ int attn_bwd_validate(const void *q, const void *k, const void *v,
  * with s and L exactly as attn_fwd. q and k are [B, H, M, D] / [B, H, N, D],
  * v is [B, H, N, Dv], o is [B, H, M, Dv], lse [B, H, M] fp32; layout,
  * ownership, execution and errors as attn_fwd. Dv == D is attn_fwd itself
- * (every dtype). Dv != D: MI355_ATTN_FP32 with D and Dv each in
- * {16, 32, 64, 128}, or MI355_ATTN_BF16 / MI355_ATTN_FP16 with
- * (D, Dv) = (64, 128) or (128, 64); anything else returns
- * MI355_ATTN_ERR_UNSUPPORTED.
+ * (every dtype). Dv != D: every dtype, D and Dv each in {16, 32, 64, 128};
+ * other head dims return MI355_ATTN_ERR_UNSUPPORTED.
  */
 int attn_fwd_dv(const void *q, const void *k, const void *v, void *o, float *lse,
                 int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, int64_t Dv,

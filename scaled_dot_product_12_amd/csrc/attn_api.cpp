@@ -203,12 +203,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 // Checks of attn_fwd_dv when the value head dim differs from D: v is
-// [B,H,N,Dv] and o [B,H,M,Dv]; fp32 for D, Dv in {16, 32, 64, 128}, bf16 and
-// fp16 for (D, Dv) = (64, 128) or (128, 64).
+// [B,H,N,Dv] and o [B,H,M,Dv]; D and Dv each in {16, 32, 64, 128}, any dtype.
 static bool dv_pair_supported(int64_t D, int64_t Dv, int dtype) {
-  if (!supported_d(D) || !supported_d(Dv)) return false;
-  if (dtype == MI355_ATTN_FP32) return true;
-  return (D == 64 && Dv == 128) || (D == 128 && Dv == 64);
+  (void)dtype;
+  return supported_d(D) && supported_d(Dv);
 }
 
 static int validate_dv(const void* q, const void* k, const void* v, const void* o,

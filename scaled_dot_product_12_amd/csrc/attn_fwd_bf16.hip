@@ -555,20 +555,26 @@ static hipError_t launch_16_dispatch(const LaunchArgs& a) {
   return pos ? launch_16_d<D, DV, false, true, F16>(a) : launch_16_d<D, DV, false, false, F16>(a);
 }
 
-// Equal head dims in {16, 32, 64, 128}; a value head dim of its own for the
-// pairs (64, 128) and (128, 64).
+template <int D, bool F16>
+static hipError_t launch_16_dv(const LaunchArgs& a) {
+  switch (a.Dv) {
+    case 16: return launch_16_dispatch<D, 16, F16>(a);
+    case 32: return launch_16_dispatch<D, 32, F16>(a);
+    case 64: return launch_16_dispatch<D, 64, F16>(a);
+    case 128: return launch_16_dispatch<D, 128, F16>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Head dims D and Dv each in {16, 32, 64, 128} (Dv = D unless v has a head
+// dim of its own).
 template <bool F16>
 static hipError_t launch_main_16(const LaunchArgs& a) {
-  if (a.Dv != a.D) {
-    if (a.D == 64 && a.Dv == 128) return launch_16_dispatch<64, 128, F16>(a);
-    if (a.D == 128 && a.Dv == 64) return launch_16_dispatch<128, 64, F16>(a);
-    return hipErrorInvalidValue;
-  }
   switch (a.D) {
-    case 16: return launch_16_dispatch<16, 16, F16>(a);
-    case 32: return launch_16_dispatch<32, 32, F16>(a);
-    case 64: return launch_16_dispatch<64, 64, F16>(a);
-    case 128: return launch_16_dispatch<128, 128, F16>(a);
+    case 16: return launch_16_dv<16, F16>(a);
+    case 32: return launch_16_dv<32, F16>(a);
+    case 64: return launch_16_dv<64, F16>(a);
+    case 128: return launch_16_dv<128, F16>(a);
     default: return hipErrorInvalidValue;
   }
 }

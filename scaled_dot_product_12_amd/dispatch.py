@@ -97,10 +97,8 @@ def sdpa_checker(query, key, value, attn_mask=None, dropout_p: float = 0.0,
     if D not in FWD_HEAD_DIMS:
         return False, f"head dim {D} is not supported ({FWD_HEAD_DIMS})"
     Dv = value.shape[3]
-    if Dv != D and not ((query.dtype == torch.float32 and Dv in FWD_HEAD_DIMS)
-                        or (D, Dv) in ((64, 128), (128, 64))):
-        return False, (f"a value head dim other than the query's needs float32 inputs with "
-                       f"Dv in {FWD_HEAD_DIMS}, or (D, Dv) = (64, 128) or (128, 64)")
+    if Dv != D and Dv not in FWD_HEAD_DIMS:
+        return False, f"value head dim {Dv} is not supported ({FWD_HEAD_DIMS})"
     if M > 0 and key.shape[2] == 0:
         return False, "no keys"
     if scale is not None and not math.isfinite(float(scale)):

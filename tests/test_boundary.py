@@ -252,10 +252,9 @@ def test_fwd_dv_validation(hip_lib):
     assert dv() == OK
     assert dv(D=128, Dv=16) == OK
     assert dv(Dv=64, dtype=BF16) == OK                 # equal dims: any dtype
-    assert dv(dtype=BF16) == OK                        # (64, 128) in 16 bits
-    assert dv(D=128, Dv=64, dtype=FP16) == OK
-    assert dv(D=32, Dv=64, dtype=BF16) == UNSUPPORTED  # other 16-bit pairs
-    assert dv(D=128, Dv=16, dtype=FP16) == UNSUPPORTED
+    assert dv(dtype=BF16) == OK                        # every pair in 16 bits too
+    assert dv(D=128, Dv=16, dtype=FP16) == OK
+    assert dv(D=32, Dv=96, dtype=BF16) == UNSUPPORTED
     assert dv(Dv=48) == UNSUPPORTED
     assert dv(Dv=0) == INVALID
     assert dv(N=0) == INVALID

@@ -122,8 +122,8 @@ def test_checker_on_gpu_tensors(hip_lib):
 
 @pytest.mark.gpu
 def test_sdpa_dropin_value_head_dim_of_its_own(hip_lib):
-    """fp32 with Dv != D runs (attn_fwd_dv, same result as the binding); other
-    dtypes and gradient requests are refused with the reason."""
+    """Dv != D runs (attn_fwd_dv, same result as the binding); an unsupported
+    Dv and gradient requests are refused with the reason."""
     d = _dispatch()
     q, k, _ = _gpu(*make_qkv(2, 3, 90, 120, 64, "fp32", seed=66))
     (v,) = _gpu(make_qkv(2, 3, 90, 120, 32, "fp32", seed=67)[2])
@@ -133,8 +133,9 @@ def test_sdpa_dropin_value_head_dim_of_its_own(hip_lib):
         ref, _ = hip_lib.attn_fwd(q, k, v, is_causal=True)
     torch.cuda.synchronize()
     assert tuple(o.shape) == (2, 3, 90, 32) and torch.equal(o, ref)
-    ok, why = d.sdpa_checker(q.bfloat16(), k.bfloat16(), v.bfloat16())
-    assert not ok and "float32" in why
+    assert d.sdpa_checker(q.bfloat16(), k.bfloat16(), v.bfloat16())[0]
+    ok, why = d.sdpa_checker(q, k, v[..., :24].contiguous())
+    assert not ok and "value head dim" in why
     q.requires_grad_(True)
     ok, why = d.sdpa_checker(q, k, v)
     assert not ok and "backward" in why

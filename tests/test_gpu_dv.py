@@ -1,7 +1,7 @@
 """GPU parity of attention with a value head dim of its own (attn_fwd_dv):
 the HIP path against oracle.attn_fwd_dv on every element, at the fp32 bounds
-(|dO| <= 2e-5, |dL| <= 1e-5) and, for the 16-bit pairs (64, 128) and
-(128, 64), at the bf16 / fp16 bounds with the oracle on the rounded inputs. The shapes span several key tiles with
+(|dO| <= 2e-5, |dL| <= 1e-5) and, for 16-bit inputs, at the bf16 / fp16
+bounds with the oracle on the rounded inputs. The shapes span several key tiles with
 ragged tails and the three key-split settings of the fp32 kernel (problems
 with few, some and many 32-row blocks)."""
 import numpy as np
@@ -75,8 +75,11 @@ def test_dv_empty_queries():
     assert tuple(o.shape) == (1, 2, 0, 64) and lse.numel() == 0
 
 
+PAIRS16 = [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128) if a != b]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("D,Dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("D,Dv", PAIRS16)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 300, 200), (1, 2, 65, 1), (1, 1, 513, 700)])
 def test_dv_16bit_matches_oracle(dtype, D, Dv, causal, shape):
