@@ -151,9 +151,8 @@ def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
              out: Optional[Tuple] = None,
              path: int = MI355_ATTN_PATH_AUTO):
     """(O, L) = attention forward of GPU tensors q [B,H,M,D], k [B,H,N,D],
-    v [B,H,N,Dv] (Dv = D; or, through the C attn_fwd_dv, any other of 16, 32,
-    64, 128 for fp32 and (D, Dv) = (64, 128) or (128, 64) for bf16 / fp16:
-    O is then [B,H,M,Dv]).
+    v [B,H,N,Dv] (Dv = D, or through the C attn_fwd_dv any other of 16, 32,
+    64, 128: O is then [B,H,M,Dv]).
 
     O has q's dtype; L is fp32 [B,H,M], natural log. ``scale`` defaults to
     1/sqrt(D). ``out=(o, lse)`` writes into preallocated tensors. ``path``
