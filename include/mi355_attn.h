@@ -249,6 +249,16 @@ int axial_pass_validate(const float *x, const float *out, const float *ln_w,
                         const float *b_out, int64_t B, int64_t Hh, int64_t W,
                         int64_t C, int64_t heads, int axis, float eps);
 
+/* axial_pass_split -- workgroups per sequence of the launch axial_pass makes
+ * for this image and axis: 2 when the pass has at most 128 sequences and
+ * out != x (each of the two takes half of the query tokens and projects keys
+ * and values for all of them), else 1. An in-place pass never splits: one
+ * half would read tokens the other half has already overwritten. Returns -1
+ * for an invalid axis, negative or empty sizes, or a sequence length above
+ * 64. Pure host logic: no HIP call, no dereference. */
+int axial_pass_split(const float *x, const float *out, int64_t B, int64_t Hh,
+                     int64_t W, int axis);
+
 /* axial_block -- the whole block: the row pass from x into out with the
  * row_* weights, then the column pass on out, in place, with the col_*
  * weights (the column pass attends over the row pass's result). Two

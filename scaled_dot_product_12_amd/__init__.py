@@ -44,7 +44,7 @@ MI355_AXIAL_COL = 1
 EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
            "attn_fwd_select_path", "attn_status_string", "attn_bwd",
            "attn_bwd_validate", "axial_pass", "axial_pass_validate", "axial_block",
-           "attn_fwd_dv", "attn_fwd_dv_validate")
+           "attn_fwd_dv", "attn_fwd_dv_validate", "axial_pass_split")
 
 _lib = None
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.axial_pass.restype = cint
         L.axial_pass_validate.argtypes = [vp] * 7 + [i64] * 5 + [cint, ctypes.c_float]
         L.axial_pass_validate.restype = cint
+        L.axial_pass_split.argtypes = [vp, vp, i64, i64, i64, cint]
+        L.axial_pass_split.restype = cint
         L.axial_block.argtypes = [vp] * 12 + [i64] * 5 + [ctypes.c_float, vp]
         L.axial_block.restype = cint
         L.attn_status_string.argtypes = [cint]
@@ -251,6 +253,12 @@ def axial_pass_validate(x, out, ln_w, ln_b, w_qkv, w_out, b_out, B, Hh, W, C, he
     """The C checks of axial_pass on raw pointers (integers); no launch."""
     return lib().axial_pass_validate(x, out, ln_w, ln_b, w_qkv, w_out, b_out, B, Hh, W, C,
                                      heads, int(axis), float(eps))
+
+
+def axial_pass_split(x, out, B, Hh, W, axis) -> int:
+    """Workgroups per sequence of axial_pass's launch (2 or 1; -1 if invalid);
+    x and out are addresses (integers). Host logic only."""
+    return lib().axial_pass_split(x, out, B, Hh, W, int(axis))
 
 
 def _check_axial(x, params, out):

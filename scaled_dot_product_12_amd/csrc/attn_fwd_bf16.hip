@@ -161,8 +161,9 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D > DV ? D : DV)) vo
   const int qi = qw0 + r32;  // this lane's query row
 
   // Key tiles the workgroup visits. Under the causal mask a wave may visit
-  // up to two tiles that are fully masked for its rows; they contribute
-  // exact zeros.
+  // up to three tiles that are fully masked for its rows (wave 0 of a
+  // 256-row tile: keys 64 .. 255 past the tile's first row); they
+  // contribute exact zeros.
   int nt = (N + BN - 1) / BN;
   if (CAUSAL) nt = min(nt, (min(q_wg0 + BM, M) - 1) / BN + 1);
 

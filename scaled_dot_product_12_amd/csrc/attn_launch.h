@@ -15,7 +15,7 @@ struct LaunchArgs {
   float* lse;
   int64_t BH;  // B * H
   int64_t M, N, D;
-  int64_t Dv;  // value and output head dim (equals D except on the fp32 main path)
+  int64_t Dv;  // value and output head dim (equals D unless v has a head dim of its own)
   float scale;
   bool causal;
   hipStream_t stream;
@@ -78,5 +78,8 @@ struct AxialLaunchArgs {
 
 // One residual axial-attention pass (C = 64 features, 4 heads of 16).
 hipError_t launch_axial_pass(const AxialLaunchArgs& a);
+// Workgroups per sequence that launch_axial_pass uses: 2 for at most 128
+// sequences read from one buffer and written to another, else 1 (in place).
+int axial_split(int64_t nseq, const float* x, const float* out);
 
 }  // namespace mi355

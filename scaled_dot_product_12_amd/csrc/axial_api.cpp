@@ -135,6 +135,16 @@ int axial_pass(const float* x, float* out, const float* ln_w, const float* ln_b,
   return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 
+int axial_pass_split(const float* x, const float* out, int64_t B, int64_t Hh, int64_t W,
+                     int axis) {
+  if (B < 0 || Hh < 0 || W < 0) return -1;
+  int64_t bh, tokens;
+  if (!mul_ok(B, Hh, &bh) || !mul_ok(bh, W, &tokens) || tokens == 0) return -1;
+  if (check_axis(B, Hh, W, axis) != MI355_ATTN_OK) return -1;
+  const int64_t nseq = B * (axis == MI355_AXIAL_ROW ? Hh : W);
+  return mi355::axial_split(nseq, x, out);
+}
+
 int axial_block(const float* x, float* out, const float* row_ln_w, const float* row_ln_b,
                 const float* row_w_qkv, const float* row_w_out, const float* row_b_out,
                 const float* col_ln_w, const float* col_ln_b, const float* col_w_qkv,

@@ -5,10 +5,11 @@
 // image columns of the row pass's output).
 //
 // One workgroup (4 waves) per sequence of L <= 64 tokens with C = 64 features
-// and 4 heads of 16, or, when there are fewer sequences than CUs, two
-// workgroups per sequence that each take half of its query tokens (both
-// project K and V for every token; Q, the attention rows, the output
-// projection and the store are split). Everything between the token load and
+// and 4 heads of 16, or, when there are fewer sequences than CUs and the
+// pass writes a buffer other than the one it reads, two workgroups per
+// sequence that each take half of its query tokens (both project K and V for
+// every token; Q, the attention rows, the output projection and the store are
+// split). Everything between the token load and
 // the final store stays in LDS and registers:
 //  * the tokens are gathered straight from the image tensor with the pass's
 //    strides (the column pass needs no transposed copy);
@@ -108,8 +109,11 @@ __global__ __launch_bounds__(kWaves * 64) void axial_pass_kernel(
     h = wg % QS;
   }
   const int q0 = h * QRB;  // first query block
-  // x and out may be the same buffer: a workgroup reads all of its tokens
-  // before it writes any, and sequences are disjoint.
+  // x and out may be the same buffer only in the unsplit launch (QS = 1): a
+  // workgroup reads all of its tokens before it writes any, and sequences are
+  // disjoint. The two halves of a split sequence both read every token of it
+  // while each writes half of them, so the host never splits a pass whose
+  // output is its input.
   const int64_t base = (int64_t)(s / inner) * outer_stride + (int64_t)(s % inner) * inner_stride;
 
   // Tokens first (16 threads per token, one 16-byte chunk of 4 features
@@ -272,13 +276,18 @@ void launch_lp(const AxialLaunchArgs& a, float c) {
 
 // Query split: two workgroups per sequence while that still leaves at most
 // one per CU (256 CUs); the K and V projections they both do cost less than
-// the idle CUs would.
+// the idle CUs would. Never in place: each half reads all tokens of the
+// sequence, which the other half's stores would otherwise overwrite.
 constexpr int64_t kSplitBelow = 256 / 2;
+
+int axial_split(int64_t nseq, const float* x, const float* out) {
+  return (nseq <= kSplitBelow && x != out) ? 2 : 1;
+}
 
 hipError_t launch_axial_pass(const AxialLaunchArgs& a) {
   // softmax in base 2: scores scaled by log2(e) / sqrt(head dim)
   const float c = (float)(1.4426950408889634 / 4.0);
-  const bool split = a.nseq <= kSplitBelow;
+  const bool split = axial_split(a.nseq, a.x, a.out) == 2;
   if (a.L <= 32) {
     if (split) launch_lp<32, 2>(a, c);
     else launch_lp<32, 1>(a, c);

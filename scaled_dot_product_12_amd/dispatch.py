@@ -9,11 +9,21 @@ attention op and a drop-in for ``torch.nn.functional.scaled_dot_product_attentio
   implements that call, with the reason when it does not -- the checker of
   "Extend Thunder with CUDA-Python" (registering the kernel as an
   implementation of torch SDPA), extended to what the kernels here support
-  (the causal mask, bf16 and fp32 forward, bf16 backward).
+  (the causal mask; fp32, bf16 and fp16 forward; bf16 and fp16 backward).
 * ``scaled_dot_product_attention`` has torch's signature; it runs the
   library's kernels when the checker accepts and raises NotImplementedError
   with the checker's reason otherwise. There is no silent fallback to another
   implementation.
+* ``route_sdpa()`` is a context manager (a ``TorchFunctionMode``) under
+  which every call of ``torch.nn.functional.scaled_dot_product_attention``
+  made by unmodified user code -- a model's attention layer -- is offered to
+  the checker and, when accepted, runs on the library's kernels: the
+  executor / checker / implementation registration that "Extend Thunder with
+  CUDA-Python" ("Running our kernel in Thunder") performs for its own
+  kernel. A call the checker rejects raises NotImplementedError with the
+  reason (``strict=True``, the default), or, with ``strict=False``, goes on
+  to torch's own SDPA, as Thunder hands an operation its checker declines to
+  the next executor in the list.
 
 Inputs that are not contiguous are copied to contiguous [B, H, seq, D]
 tensors first (a layout copy by torch; every step of the attention itself
@@ -25,6 +35,7 @@ import math
 from typing import Optional, Tuple
 
 import torch
+from torch.overrides import TorchFunctionMode
 
 from . import attn_bwd, attn_fwd
 
@@ -63,7 +74,7 @@ def attention_with_lse(q, k, v, is_causal: bool = False,
 
 def attention(q, k, v, is_causal: bool = False, scale: Optional[float] = None) -> torch.Tensor:
     """O = softmax(scale q k^T [+ causal mask]) v for [B, H, seq, D] GPU
-    tensors, differentiable in q, k, v (backward: bf16, D in 32/64/128)."""
+    tensors, differentiable in q, k, v (backward: bf16 or fp16, D in 32/64/128)."""
     return _Attention.apply(q, k, v, bool(is_causal), scale)[0]
 
 
@@ -123,3 +134,58 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p: f
     if not ok:
         raise NotImplementedError(f"scaled_dot_product_attention: {why}")
     return attention(query, key, value, is_causal=is_causal, scale=scale)
+
+
+_SDPA_ARGS = ("query", "key", "value", "attn_mask", "dropout_p", "is_causal", "scale",
+              "enable_gqa")
+_SDPA_DEFAULTS = {"attn_mask": None, "dropout_p": 0.0, "is_causal": False, "scale": None,
+                  "enable_gqa": False}
+
+
+def _sdpa_call_args(args, kwargs) -> dict:
+    """torch's SDPA arguments as one name -> value dict (positional or keyword)."""
+    if len(args) > len(_SDPA_ARGS):
+        raise TypeError("scaled_dot_product_attention: too many positional arguments")
+    out = dict(_SDPA_DEFAULTS)
+    out.update(zip(_SDPA_ARGS, args))
+    for name, val in kwargs.items():
+        if name not in _SDPA_ARGS:
+            raise TypeError(f"scaled_dot_product_attention: unexpected argument {name!r}")
+        out[name] = val
+    return out
+
+
+class route_sdpa(TorchFunctionMode):
+    """While active, ``torch.nn.functional.scaled_dot_product_attention``
+    calls run on this library when ``sdpa_checker`` accepts them.
+
+    ``strict=True``: a rejected call raises NotImplementedError with the
+    checker's reason. ``strict=False``: it runs torch's own SDPA instead.
+    ``routed`` and ``declined`` count the calls of each kind. Every other
+    torch function passes through unchanged. Calls that torch makes from
+    inside another function that this mode sees first (for example the
+    functional forward of ``nn.MultiheadAttention``) run with the mode
+    suspended, as torch suspends a mode while its handler runs, and are not
+    routed.
+    """
+
+    def __init__(self, strict: bool = True):
+        super().__init__()
+        self.strict = strict
+        self.routed = 0
+        self.declined = 0
+
+    def __torch_function__(self, func, types, args=(), kwargs=None):
+        kwargs = kwargs or {}
+        if func is not torch.nn.functional.scaled_dot_product_attention:
+            return func(*args, **kwargs)
+        a = _sdpa_call_args(args, kwargs)
+        ok, why = sdpa_checker(**a)
+        if not ok:
+            if self.strict:
+                raise NotImplementedError(f"scaled_dot_product_attention: {why}")
+            self.declined += 1
+            return func(*args, **kwargs)
+        self.routed += 1
+        return attention(a["query"], a["key"], a["value"], is_causal=bool(a["is_causal"]),
+                         scale=a["scale"])

@@ -58,6 +58,8 @@ int main(void) {
   expect("axial_pass_validate C=32", axial_pass_validate(x, out, w[0], w[1], w[2], w[3], w[4], 4,
                                                          32, 32, 32, 4, MI355_AXIAL_COL, 1e-5f),
          MI355_ATTN_ERR_UNSUPPORTED);
+  expect("axial_pass_split out of place", axial_pass_split(x, out, 4, 32, 32, MI355_AXIAL_COL), 2);
+  expect("axial_pass_split in place", axial_pass_split(out, out, 4, 32, 32, MI355_AXIAL_COL), 1);
   expect("axial_block empty", axial_block(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 32, 32, 64, 4,
                                           1e-5f, 0),
          MI355_ATTN_OK);

@@ -91,3 +91,29 @@ def test_block_checks_both_passes_before_any_launch(hip_lib):
     assert b(col=(OUT,) + tuple(COL_W[1:])) == INVALID   # column weights inside out
     assert b(out=X + 16) == INVALID
     assert b(B=0, x=0, out=0) == OK          # empty: nothing launched
+
+
+def test_in_place_pass_never_splits(hip_lib):
+    """A pass with at most 128 sequences splits each over two workgroups that
+    both read every token of it; in place (out == x) one half would read
+    tokens the other has already overwritten, so the launch must not split."""
+    split = hip_lib.axial_pass_split
+    # The page's images: 4 x 32 x 32, 128 sequences per pass.
+    assert split(X, OUT, 4, 32, 32, ROW) == 2
+    assert split(X, OUT, 4, 32, 32, COL) == 2
+    assert split(X, X, 4, 32, 32, ROW) == 1
+    assert split(X, X, 4, 32, 32, COL) == 1
+    # More sequences than half the CUs: never split.
+    assert split(X, OUT, 8, 32, 32, ROW) == 1
+    assert split(X, OUT, 2, 100, 64, ROW) == 1
+    # Every small shape: in place is always 1.
+    for B, Hh, W in ((1, 1, 1), (1, 64, 1), (3, 7, 45), (4, 32, 32), (1, 2, 64)):
+        for axis in (ROW, COL):
+            assert split(X, X, B, Hh, W, axis) == 1
+            assert split(X, OUT, B, Hh, W, axis) in (1, 2)
+    # Invalid: axis, negative or empty sizes, sequence longer than 64.
+    assert split(X, OUT, 4, 32, 32, 2) == -1
+    assert split(X, OUT, -1, 32, 32, ROW) == -1
+    assert split(X, OUT, 0, 32, 32, ROW) == -1
+    assert split(X, OUT, 1, 1, 65, ROW) == -1
+    assert split(X, OUT, 1, 65, 1, COL) == -1

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
          "attn_status_string", "attn_bwd", "attn_bwd_validate", "axial_pass",
-         "axial_pass_validate", "axial_block", "attn_fwd_dv", "attn_fwd_dv_validate"])
+         "axial_pass_validate", "axial_block", "attn_fwd_dv", "attn_fwd_dv_validate",
+         "axial_pass_split"])
 
 
 def test_library_exports_every_declared_symbol(hip_lib):
@@ -265,3 +266,4 @@ def test_fwd_dv_validation(hip_lib):
     vbytes = 2 * 3 * 70 * 128 * 4
     assert dv(ptrs=[P[0], P[1], P[2], P[2] + vbytes - 16, P[4]]) == INVALID
     assert dv(ptrs=[P[0], P[1], P[2], P[2] + vbytes, P[4]]) == OK
+

@@ -30,6 +30,43 @@ def test_checker_rejections_on_cpu(hip_lib):
         d.scaled_dot_product_attention(q, q, q)
 
 
+class _SdpaBlock(torch.nn.Module):
+    """An attention layer written against torch's own SDPA, as model code is:
+    it knows nothing of this library."""
+
+    def __init__(self, causal):
+        super().__init__()
+        self.causal = causal
+
+    def forward(self, q, k, v):
+        return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=self.causal)
+
+
+def test_route_sdpa_intercepts_torch_sdpa_on_cpu(hip_lib):
+    """The mode sees the module's torch SDPA call: strict, the checker's
+    reason is raised (CPU tensors are not the library's); non-strict, torch's
+    own SDPA runs and gives its usual result. Other torch calls are untouched."""
+    d = _dispatch()
+    q, k, v = make_qkv(1, 2, 9, 11, 16, "fp32", seed=3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    blk = _SdpaBlock(causal=True)
+    with d.route_sdpa() as mode:
+        assert torch.equal(q + 1, q.add(1))
+        with pytest.raises(NotImplementedError, match="not on a GPU"):
+            blk(q, k, v)
+        with pytest.raises(NotImplementedError, match="attn_mask"):
+            torch.nn.functional.scaled_dot_product_attention(q, k, v, torch.ones(9, 11) > 0)
+    assert mode.routed == 0
+    with d.route_sdpa(strict=False) as mode:
+        out = blk(q, k, v)
+        out2 = torch.nn.functional.scaled_dot_product_attention(q, k, v, None, 0.0, True)
+    assert torch.equal(out, ref) and torch.equal(out2, ref)
+    assert (mode.routed, mode.declined) == (0, 2)
+    with pytest.raises(TypeError):
+        with d.route_sdpa():
+            torch.nn.functional.scaled_dot_product_attention(q, k, v, bogus=1)
+
+
 
 
 def _gpu(*ts):
@@ -139,3 +176,34 @@ def test_sdpa_dropin_value_head_dim_of_its_own(hip_lib):
     q.requires_grad_(True)
     ok, why = d.sdpa_checker(q, k, v)
     assert not ok and "backward" in why
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "fp32", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_route_sdpa_runs_an_unmodified_module_on_the_library(hip_lib, dtype, causal):
+    """A module that calls torch's SDPA, run under route_sdpa: its output is
+    bit-equal to attn_fwd's, and (16-bit) its gradients to attn_bwd's."""
+    d = _dispatch()
+    q0, k0, v0 = make_qkv(2, 4, 300, 257, 128, dtype, seed=68)
+    blk = _SdpaBlock(causal)
+    q, k, v = _gpu(q0, k0, v0)
+    with torch.no_grad():
+        ref_o, lse = hip_lib.attn_fwd(q, k, v, is_causal=causal)
+        with d.route_sdpa() as mode:
+            o = blk(q, k, v)
+    torch.cuda.synchronize()
+    assert mode.routed == 1 and torch.equal(o, ref_o)
+    if dtype == "fp32":
+        return
+    g = make_dout(2, 4, 300, 128, dtype, seed=68).to("cuda:0")
+    qg, kg, vg = (t.clone().requires_grad_(True) for t in (q, k, v))
+    with d.route_sdpa() as mode:
+        o = blk(qg, kg, vg)
+    o.backward(g)
+    with torch.no_grad():
+        ref = hip_lib.attn_bwd(q, k, v, ref_o, lse, g, is_causal=causal)
+    torch.cuda.synchronize()
+    assert mode.routed == 1 and torch.equal(o.detach(), ref_o)
+    for got, r in zip((qg.grad, kg.grad, vg.grad), ref):
+        assert torch.equal(got, r)

@@ -105,3 +105,23 @@ def test_zero_output_projection_is_exact_residual():
         got = attn.axial_pass(xd, pd, axis)
         torch.cuda.synchronize()
         assert torch.equal(got, xd)
+
+
+def test_random_image_sweep():
+    """40 seeded random images (B 1..6, Hh and W 1..64: both sequence
+    paddings, split and unsplit launches), each pass out of place and in
+    place, every element against the oracle."""
+    rng = np.random.default_rng(606)
+    for case in range(40):
+        B, Hh, W = int(rng.integers(1, 7)), int(rng.integers(1, 65)), int(rng.integers(1, 65))
+        x, row, col = make_axial_block(B, Hh, W, 64, seed=700 + case)
+        print(f"[axial-sweep] case {case} shape={(B, Hh, W)}", flush=True)
+        xd, rd, cd = _dev(x, row, col)
+        for axis, name, p, pd in ((ROW, "row", row, rd), (COL, "col", col, cd)):
+            want = ax.axial_pass(x, p, name, 4)
+            got = attn.axial_pass(xd, pd, axis)
+            y = xd.clone()
+            attn.axial_pass(y, pd, axis, out=y)
+            torch.cuda.synchronize()
+            assert _err(got, want) <= TOL, (case, name)
+            assert _err(y, want) <= TOL, (case, name, "in place")

@@ -13,7 +13,7 @@ import torch
 
 import scaled_dot_product_12_amd as attn
 from scaled_dot_product_12_amd.inputs import WORKLOADS, make_qkv, workload_inputs
-from parity_util import TDT, TOL, check_full, check_sampled, run_gpu
+from parity_util import TDT, TOL, check_full, check_full_large, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -88,15 +88,16 @@ def test_workload_full(name):
         check_full(q, k, v, w.causal, w.scale, path=MAIN, label=name + "-main")
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["c4", "c5", "p64", "p128", "c4h"])
-def test_workload_sampled(name):
+def test_workload_full_large(name):
+    """The long-context 16-bit workloads at their full sizes, in the launch the
+    benchmark times: every element of O and L against the full fp64 oracle
+    (all host cores; up to ~1 min for the 4x32x8192^2x128 shape)."""
     w = WORKLOADS[name]
     q, k, v = workload_inputs(w)
-    o, lse = check_sampled(q, k, v, w.causal, w.scale, n_random=400, seed=w.seed,
-                           label=name)
-    # Properties that hold for every row at full size: finite, and the
-    # oracle's bound max_j s_ij <= L_i <= max_j s_ij + ln|J_i| for row 0 of
-    # each head where the causal row 0 has a single key.
+    o, lse = check_full_large(q, k, v, w.causal, w.scale, label=name)
+    # Causal row 0 sees key 0 only: O = v_0 and L = scale q_0.k_0 exactly.
     if w.causal:
         v0 = v[:, :, 0].float().numpy()
         assert np.abs(o[:, :, 0] - v0).max() <= TOL[w.dtype][0]
@@ -232,18 +233,21 @@ def test_empty_problem_launches_nothing():
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32", "fp16"])
 def test_random_problem_sweep(dtype):
-    """Seeded random problems (sizes 1..300, every supported D, causal or
-    not, scales of either sign), each compared element by element with the
-    oracle: tails, masks and the choice of kernel in many combinations."""
+    """112 seeded random problems per type (sizes 1..400, every supported D,
+    causal or not, scales of either sign up to 2/sqrt(D)), each compared
+    element by element with the oracle at the stated bounds: tails, masks and
+    the choice of kernel in many combinations (a third of them are short
+    enough for the small kernel, which the default path then takes)."""
     rng = np.random.default_rng({"bf16": 4242, "fp32": 4243, "fp16": 4244}[dtype])
-    for case in range(24):
+    for case in range(112):
         B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
-        M, N = int(rng.integers(1, 301)), int(rng.integers(1, 301))
+        hi = 65 if case % 3 == 0 else 401
+        M, N = int(rng.integers(1, hi)), int(rng.integers(1, hi))
         D = int(rng.choice([16, 32, 64, 128]))
         causal = bool(rng.integers(0, 2))
         scale = f32(rng.uniform(-1.0, 1.0) * 2.0 / math.sqrt(D))
         q, k, v = make_qkv(B, H, M, N, D, dtype, seed=5000 + case)
-        check_full(q, k, v, causal, scale, label=f"sweep{case}", magnitude_tol=True)
+        check_full(q, k, v, causal, scale, label=f"sweep{case}")
 
 
 def test_out_tensors_must_be_on_the_device():
