@@ -61,6 +61,7 @@ extern "C" {
 #define MI355_ATTN_ERR_UNSUPPORTED   2 /* valid but not implemented (D, size)      */
 #define MI355_ATTN_ERR_MISALIGNED    3 /* q/k/v/o not 16-byte or lse not 4-byte    */
 #define MI355_ATTN_ERR_HIP           4 /* the HIP launch reported an error         */
+#define MI355_ATTN_ERR_SCRATCH       5 /* B*H*M above the no-alloc scratch capacity */
 
 /* Kernel paths (attn_fwd_path / attn_fwd_select_path). */
 #define MI355_ATTN_PATH_AUTO  0 /* let the library choose                        */
@@ -189,6 +190,30 @@ int attn_bwd_validate(const void *q, const void *k, const void *v,
                       const float *delta, int64_t B, int64_t H, int64_t M,
                       int64_t N, int64_t D, float scale, int is_causal,
                       int dtype);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, results and errors as attn_bwd, without
+ * the delta workspace: delta lives in a static device array of the library
+ * that holds MI355_ATTN_NOALLOC_MAX_ROWS fp32 values (4 MiB), which every GPU
+ * the library runs on keeps until the process ends. The call makes no
+ * allocation of any kind; its first call on a device looks the array's
+ * address up once (a HIP call, no allocation).
+ *
+ * B*H*M above MI355_ATTN_NOALLOC_MAX_ROWS returns MI355_ATTN_ERR_SCRATCH
+ * (after every check attn_bwd makes, still before any HIP call) and
+ * launches nothing. Every call on one GPU shares that GPU's array, which
+ * keeps the last call's delta: calls whose work overlaps on one GPU (on
+ * different streams) race and must be ordered by the caller. Nothing in the
+ * array needs clearing: each call writes every value it reads.
+ */
+#define MI355_ATTN_NOALLOC_MAX_ROWS 1048576
+int attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                     const float *lse, const void *dout, void *dq, void *dk,
+                     void *dv, int64_t B, int64_t H, int64_t M, int64_t N,
+                     int64_t D, float scale, int is_causal, int dtype,
+                     void *stream);
 
 /* attn_fwd_dv -- attn_fwd with a value head dim Dv of its own ("Blackwell
  * Attention Example", attention kernel: v may be [.., N, Dv]):

@@ -35,6 +35,8 @@ MI355_ATTN_ERR_INVALID_ARG = 1
 MI355_ATTN_ERR_UNSUPPORTED = 2
 MI355_ATTN_ERR_MISALIGNED = 3
 MI355_ATTN_ERR_HIP = 4
+MI355_ATTN_ERR_SCRATCH = 5
+MI355_ATTN_NOALLOC_MAX_ROWS = 1048576
 MI355_ATTN_PATH_AUTO = 0
 MI355_ATTN_PATH_MAIN = 1
 MI355_ATTN_PATH_SMALL = 2
@@ -44,7 +46,8 @@ MI355_AXIAL_COL = 1
 EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
            "attn_fwd_select_path", "attn_status_string", "attn_bwd",
            "attn_bwd_validate", "axial_pass", "axial_pass_validate", "axial_block",
-           "attn_fwd_dv", "attn_fwd_dv_validate", "axial_pass_split")
+           "attn_fwd_dv", "attn_fwd_dv_validate", "axial_pass_split",
+           "attn_bwd_noalloc")
 
 _lib = None
 
@@ -72,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_select_path.restype = cint
         L.attn_bwd.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint, vp]
         L.attn_bwd.restype = cint
+        L.attn_bwd_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, cint, cint, vp]
+        L.attn_bwd_noalloc.restype = cint
         L.attn_bwd_validate.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint]
         L.attn_bwd_validate.restype = cint
         L.attn_fwd_dv.argtypes = [vp] * 5 + [i64] * 6 + [ctypes.c_float, cint, cint, vp]
@@ -245,6 +250,43 @@ def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
                             int(bool(is_causal)), dt, stream)
     if st != MI355_ATTN_OK:
         raise RuntimeError(f"attn_bwd failed: {attn_status_string(st)} ({st})")
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, out, is_causal: bool = False,
+                     scale: Optional[float] = None):
+    """attn_bwd through the C ``attn_bwd_noalloc``: no workspace argument and
+    no allocation on this path -- the caller passes ``out=(dq, dk, dv)``
+    (contiguous tensors like q, k, v) and the library keeps delta in its
+    static device array (B*H*M <= MI355_ATTN_NOALLOC_MAX_ROWS). Calls that
+    overlap on one GPU share that array and must not run concurrently."""
+    import torch
+    B, H, M, N, D = _check(q, k, v)
+    if v.shape != k.shape:
+        raise ValueError("attn_bwd_noalloc needs v with the head dim of q and k")
+    dt = _dtype_code(q)
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape)):
+        if (t.shape != shape or t.dtype != q.dtype or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if (tuple(lse.shape) != (B, H, M) or lse.dtype != torch.float32
+            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 [B, H, M] tensor on q's device")
+    dq, dk, dv = out
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if (t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError(f"out {name} must be a contiguous tensor like {name[1]}")
+    if scale is None:
+        scale = default_scale(D)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = lib().attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                    dk.data_ptr(), dv.data_ptr(), B, H, M, N, D,
+                                    float(scale), int(bool(is_causal)), dt, stream)
+    if st != MI355_ATTN_OK:
+        raise RuntimeError(f"attn_bwd_noalloc failed: {attn_status_string(st)} ({st})")
     return dq, dk, dv
 
 

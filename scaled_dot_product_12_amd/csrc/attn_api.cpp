@@ -77,10 +77,13 @@ int validate(const void* q, const void* k, const void* v, const void* o,
 
 bool bwd_supported_d(int64_t D) { return D == 32 || D == 64 || D == 128; }
 
+// own_delta: the library supplies delta (the no-alloc entry), so the delta
+// pointer is not the caller's and is not checked.
 int validate_bwd(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, const void* dq, const void* dk,
                  const void* dv, const float* delta, int64_t B, int64_t H, int64_t M,
-                 int64_t N, int64_t D, float scale, int is_causal, int dtype) {
+                 int64_t N, int64_t D, float scale, int is_causal, int dtype,
+                 bool own_delta = false) {
   if (B < 0 || H < 0 || M < 0 || N < 0 || D < 1) return MI355_ATTN_ERR_INVALID_ARG;
   if (!known_dtype(dtype)) return MI355_ATTN_ERR_INVALID_ARG;
   if (is_causal != 0 && is_causal != 1) return MI355_ATTN_ERR_INVALID_ARG;
@@ -93,7 +96,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o,
   // Key-side buffers are always used here; with no query rows the query-side
   // ones are never touched (dK = dV = 0) and may be null.
   if (!k || !v || !dk || !dv) return MI355_ATTN_ERR_INVALID_ARG;
-  if (q_rows > 0 && (!q || !o || !lse || !dout || !dq || !delta))
+  if (q_rows > 0 && (!q || !o || !lse || !dout || !dq || (!delta && !own_delta)))
     return MI355_ATTN_ERR_INVALID_ARG;
   if (dtype == MI355_ATTN_FP32 || !bwd_supported_d(D)) return MI355_ATTN_ERR_UNSUPPORTED;
 
@@ -114,14 +117,15 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o,
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
     return MI355_ATTN_ERR_MISALIGNED;
-  if (((uintptr_t)lse | (uintptr_t)delta) & 3u) return MI355_ATTN_ERR_MISALIGNED;
+  if (((uintptr_t)lse | (own_delta ? 0 : (uintptr_t)delta)) & 3u)
+    return MI355_ATTN_ERR_MISALIGNED;
 
   // Outputs (dq, dk, dv, delta) must not overlap the inputs or each other
   // (inputs may alias one another).
   const void* in_p[6] = {q, k, v, o, lse, dout};
   const int64_t in_n[6] = {q_bytes, kv_bytes, kv_bytes, q_bytes, row_bytes, q_bytes};
-  const void* out_p[4] = {dq, dk, dv, delta};
-  const int64_t out_n[4] = {q_bytes, kv_bytes, kv_bytes, row_bytes};
+  const void* out_p[4] = {dq, dk, dv, own_delta ? nullptr : delta};
+  const int64_t out_n[4] = {q_bytes, kv_bytes, kv_bytes, own_delta ? 0 : row_bytes};
   for (int a = 0; a < 4; ++a) {
     for (int b = 0; b < 6; ++b)
       if (overlap(out_p[a], out_n[a], in_p[b], in_n[b])) return MI355_ATTN_ERR_INVALID_ARG;
@@ -321,6 +325,40 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                     int is_causal, int dtype, void* stream) {
+  const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, H, M, N, D,
+                              scale, is_causal, dtype, /*own_delta=*/true);
+  if (st != MI355_ATTN_OK) return st;
+  if (B * H * (M + N) == 0) return MI355_ATTN_OK;
+  if (B * H * M > mi355::kNoallocMaxRows) return MI355_ATTN_ERR_SCRATCH;
+  float* delta = nullptr;
+  if (mi355::noalloc_delta_scratch(&delta) != hipSuccess) return MI355_ATTN_ERR_HIP;
+  mi355::BwdLaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.BH = B * H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.causal = is_causal != 0;
+  a.stream = (hipStream_t)stream;
+  const hipError_t err =
+      dtype == MI355_ATTN_FP16 ? mi355::launch_bwd_f16(a) : mi355::launch_bwd_bf16(a);
+  return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case MI355_ATTN_OK: return "ok";
@@ -328,6 +366,7 @@ const char* attn_status_string(int status) {
     case MI355_ATTN_ERR_UNSUPPORTED: return "unsupported problem";
     case MI355_ATTN_ERR_MISALIGNED: return "misaligned pointer";
     case MI355_ATTN_ERR_HIP: return "HIP launch error";
+    case MI355_ATTN_ERR_SCRATCH: return "problem exceeds the no-alloc scratch buffer";
     default: return "unknown status";
   }
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mi355_attn.h"
+
 namespace mi355 {
 
 struct LaunchArgs {
@@ -58,6 +60,12 @@ hipError_t launch_bwd_f16(const BwdLaunchArgs& a);
 // Rows per workgroup of the two backward kernels (grid sizing checks).
 int bwd_dq_tile_rows();
 int bwd_dkdv_tile_rows();
+
+// Capacity (query rows, B*H*M) of the static delta array of the no-alloc
+// backward, and the device address of that array on the current device
+// (looked up once per device; no allocation).
+constexpr int64_t kNoallocMaxRows = MI355_ATTN_NOALLOC_MAX_ROWS;
+hipError_t noalloc_delta_scratch(float** out);
 
 struct AxialLaunchArgs {
   const float* x;

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
         ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
          "attn_status_string", "attn_bwd", "attn_bwd_validate", "axial_pass",
          "axial_pass_validate", "axial_block", "attn_fwd_dv", "attn_fwd_dv_validate",
-         "axial_pass_split"])
+         "axial_pass_split", "attn_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(hip_lib):
@@ -151,7 +151,8 @@ def test_select_path(hip_lib):
 
 def test_status_strings(hip_lib):
     names = {OK: "ok", INVALID: "invalid argument", UNSUPPORTED: "unsupported problem",
-             MISALIGNED: "misaligned pointer", HIPERR: "HIP launch error"}
+             MISALIGNED: "misaligned pointer", HIPERR: "HIP launch error",
+             5: "problem exceeds the no-alloc scratch buffer"}
     for code, s in names.items():
         assert hip_lib.attn_status_string(code) == s
     assert hip_lib.attn_status_string(99) == "unknown status"
@@ -267,3 +268,30 @@ def test_fwd_dv_validation(hip_lib):
     assert dv(ptrs=[P[0], P[1], P[2], P[2] + vbytes - 16, P[4]]) == INVALID
     assert dv(ptrs=[P[0], P[1], P[2], P[2] + vbytes, P[4]]) == OK
 
+
+def test_bwd_noalloc_checks_before_any_hip_call(hip_lib):
+    """attn_bwd_noalloc: attn_bwd's argument checks, then the scratch capacity
+    (B*H*M <= MI355_ATTN_NOALLOC_MAX_ROWS), all before any HIP call (stand-in
+    addresses, never dereferenced)."""
+    L = hip_lib.lib()
+    sz = 1 << 36
+    q, k, v, o, lse, g, dq, dk, dv = ((i + 1) * sz for i in range(9))
+    cap = hip_lib.MI355_ATTN_NOALLOC_MAX_ROWS
+    assert cap == 1 << 20
+
+    def call(B, H, M, N, D=128, dtype=BF16, **kw):
+        p = dict(q=q, k=k, v=v, o=o, lse=lse, g=g, dq=dq, dk=dk, dv=dv)
+        p.update(kw)
+        return L.attn_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["lse"], p["g"], p["dq"],
+                                  p["dk"], p["dv"], B, H, M, N, D, 0.1, 0, dtype, None)
+
+    assert call(4, 32, 8193, 64) == 5            # 4*32*8193 rows > 2^20
+    assert call(1, 1, cap + 1, 64) == 5
+    assert call(0, 4, 5, 5) == OK                # nothing to do
+    assert call(1, 1, 5, 5, dq=None) == INVALID
+    assert call(1, 1, 5, 5, D=16) == UNSUPPORTED
+    assert call(1, 1, 5, 5, dtype=FP32) == UNSUPPORTED
+    assert call(1, 1, 5, 5, dq=dq + 2) == MISALIGNED
+    assert call(1, 1, 5, 5, dq=q) == INVALID     # output overlaps an input
+    # the capacity check comes after attn_bwd's own checks
+    assert call(1, 1, cap + 1, 64, dq=None) == INVALID
