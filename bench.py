@@ -280,6 +280,28 @@ def same_bytes_copy_us(nbytes: int, steps: int = 200) -> float:
     return ms * 1e3
 
 
+def same_bytes_copy_cold_us(nbytes: int, min_calls: int = 200) -> float:
+    """same_bytes_copy_us with cold caches: the copies cycle through
+    independent source/destination pairs totalling more than COLD_BYTES
+    (HIP graph), like measure_cold does for the attention calls."""
+    import torch
+    n = max(1, nbytes // 8)
+    nsets = max(2, -(-COLD_BYTES // (8 * n)))
+    pairs = [(torch.ones(n, dtype=torch.float32, device="cuda:0"),
+              torch.empty(n, dtype=torch.float32, device="cuda:0")) for _ in range(nsets)]
+    state = {"i": 0}
+
+    def fn():
+        src, dst = pairs[state["i"] % nsets]
+        state["i"] += 1
+        dst.copy_(src)
+    calls = nsets * max(1, -(-min_calls // nsets))
+    ms, _, _ = time_launches(fn, calls, 3, graph=True, spin_s=0.2, reps=3)
+    del pairs
+    torch.cuda.empty_cache()
+    return ms * 1e3
+
+
 # Bytes one pass over the cold-timing buffer sets must touch: more than the
 # 256 MB Infinity Cache plus the 8 x 4 MB of L2, so every call finds its
 # inputs evicted.
@@ -428,7 +450,7 @@ def main():
 
     extra = {}
     if not a.no_extra:
-        for name in ("c1", "c2", "c2c", "c3r", "c3c", "c5", "p64", "p128", "c4h"):
+        for name in ("c1", "c2", "c2c", "c3r", "c3c", "c3", "c5", "p64", "p128", "c4h"):
             if name == w.name:
                 continue
             x = WORKLOADS[name]
@@ -446,7 +468,7 @@ def main():
                 "timing": "HIP graph of %d calls" % steps if small else "%d calls" % steps,
                 "repeat": xst,
             }
-            if name in ("c1", "c3r", "c3c"):
+            if name in ("c1", "c3r", "c3c", "c3"):
                 cus, nsets, cst = measure_cold(x)
                 cgbs = x.algorithmic_bytes() / (cus * 1e-6) / 1e9
                 extra[name].update({
@@ -457,6 +479,10 @@ def main():
                 cus = same_bytes_copy_us(x.algorithmic_bytes())
                 extra[name]["same_bytes_copy_us"] = round(cus, 3)
                 extra[name]["frac_of_copy_rate"] = round(cus / (xms * 1e3), 4)
+                ccus = same_bytes_copy_cold_us(x.algorithmic_bytes())
+                extra[name]["same_bytes_copy_cold_us"] = round(ccus, 3)
+                extra[name]["cold_frac_of_copy_rate"] = round(
+                    ccus / extra[name]["cold_us_per_call"], 4)
 
     if not a.no_extra:
         print("[bench] extra fused axial block", file=sys.stderr, flush=True)

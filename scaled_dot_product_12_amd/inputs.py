@@ -41,7 +41,7 @@ class Workload:
     dtype: str            # "fp32", "bf16" or "fp16"
     causal: bool
     seed: int
-    axial: str = ""       # "" or "row" / "col" for the axial passes
+    axial: str = ""       # "" or "row" / "col" / "both" for the axial passes
     note: str = field(default="", compare=False)
 
     @property
@@ -79,6 +79,11 @@ WORKLOADS: Dict[str, Workload] = {
                     note="axial row pass: 4 images x 32 rows"),
     "c3c": Workload("c3c", 128, 4, 32, 32, 16, "fp32", False, 3, axial="col",
                     note="axial column pass: 4 images x 32 columns"),
+    # Both passes in one launch: the row gather and the column gather of the
+    # same image tensors stacked along the batch ([256, 4, 32, 16]); the two
+    # passes are independent once Q, K and V are gathered.
+    "c3": Workload("c3", 256, 4, 32, 32, 16, "fp32", False, 3, axial="both",
+                   note="axial row and column passes in one launch"),
     "c4": Workload("c4", 4, 16, 4096, 4096, 128, "bf16", False, 4,
                    note="long-sequence bf16"),
     "c5": Workload("c5", 2, 32, 8192, 8192, 128, "bf16", True, 5,
@@ -150,6 +155,9 @@ def workload_inputs(w: Workload):
     """The seeded CPU tensors (q, k, v) for a named workload."""
     if w.axial:
         qi, ki, vi = make_axial(w.seed)
+        if w.axial == "both":
+            return tuple(torch.cat([axial_rows(t), axial_cols(t)], 0).contiguous()
+                         for t in (qi, ki, vi))
         f = axial_rows if w.axial == "row" else axial_cols
         return f(qi), f(ki), f(vi)
     return make_qkv(w.B, w.H, w.M, w.N, w.D, w.dtype, w.seed)

@@ -79,7 +79,7 @@ def test_scale_values(dtype, scale):
 
 
 # ---------------------------------------------------------- the workloads
-@pytest.mark.parametrize("name", ["c1", "c2", "c2c", "c3r", "c3c"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c2c", "c3r", "c3c", "c3"])
 def test_workload_full(name):
     w = WORKLOADS[name]
     q, k, v = workload_inputs(w)
