@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # fp32 (vector and MFMA)
 PEAK_HBM_GBS = 8000.0       # HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 (e4m3) MFMA
 
 
 def parse():
@@ -336,6 +337,33 @@ def measure_cold(w, min_calls: int = 200):
     return ms * 1e3, nsets, st
 
 
+def measure_fp8(steps: int = 30):
+    """The long-sequence shape with fp8 (e4m3) inputs through attn_fwd_fp8 (V
+    transposed, P rounded to fp8 for the second product, bf16 O): FLOPs
+    4*B*H*M*N*D against the 5.0 PF dense fp8 peak."""
+    import torch
+    import scaled_dot_product_12_amd as attn
+    from scaled_dot_product_12_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["c4f8"]
+    dev = torch.device("cuda:0")
+    q, k, v = workload_inputs(w)
+    qd, kd = q.to(dev), k.to(dev)
+    vtd = v.transpose(-1, -2).contiguous().to(dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def fn():
+        attn.attn_fwd_fp8(qd, kd, vtd, is_causal=w.causal, scale=w.scale, out=(o, lse))
+    ms, _, st = time_launches(fn, steps, 3)
+    tf = w.flops / (ms * 1e-3) / 1e12
+    gbs = w.algorithmic_bytes() / (ms * 1e-3) / 1e9
+    return {"c4f8": {"workload": w.describe() + " (vt transposed, bf16 O)",
+                     "us_per_call": round(ms * 1e3, 3), "tflops": round(tf, 3),
+                     "frac_compute_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "peak_tflops": PEAK_FP8_TFLOPS, "gbs": round(gbs, 1),
+                     "timing": "%d calls" % steps, "repeat": st}}
+
+
 def measure_dv(steps: int = 30):
     """Attention with a value head dim of its own, Dv = 64 beside D = 128: on
     the Thunder notebook's fp32 batch (96 x 512 x 512) and on the
@@ -489,6 +517,8 @@ def main():
         extra.update(measure_axial_block())
         print("[bench] extra value head dim of its own", file=sys.stderr, flush=True)
         extra.update(measure_dv())
+        print("[bench] extra fp8 inputs", file=sys.stderr, flush=True)
+        extra.update(measure_fp8())
 
     if not a.no_extra:
         for name in ("c4", "c5", "p64", "c4h"):

@@ -215,6 +215,39 @@ int attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
                      int64_t D, float scale, int is_causal, int dtype,
                      void *stream);
 
+/*
+ * attn_fwd_fp8 -- attn_fwd with fp8 inputs ("Blackwell Attention Example",
+ * attention kernel: P is cast to the value dtype before the second product,
+ * and fp8 values in their natural layout are noted there as Blackwell-only,
+ * so fp8 V is taken transposed):
+ *
+ *   q          [B, H, M, D] OCP e4m3 (1 sign, 4 exponent bits with bias 7,
+ *              3 mantissa bits; 0x7f / 0xff are NaN), device memory.
+ *   k          [B, H, N, D] e4m3.
+ *   vt         [B, H, D, N] e4m3: V transposed (vt[b,h,d,j] = v[b,h,j,d]).
+ *   o          [B, H, M, D] bf16 output.
+ *   lse        [B, H, M] fp32 output, natural log.
+ *
+ * Both products run in e4m3 with fp32 accumulation; P is rounded to e4m3
+ * (nearest even) before the second one, and the row sum is taken from the
+ * same rounded P, so O is an exact convex combination of value rows up to
+ * fp32 accumulation; O is rounded to bf16 on the store. Scores, masking,
+ * scale and L as attn_fwd. Supported: D in {64, 128} and N a multiple of 16
+ * (else UNSUPPORTED); q, k, vt and o 16-byte aligned, lse 4-byte aligned
+ * (MISALIGNED); o and lse must not overlap the inputs or each other
+ * (INVALID_ARG). Other argument rules, ownership, execution and errors as
+ * attn_fwd; B*H*M == 0 returns OK without launching.
+ */
+int attn_fwd_fp8(const void *q, const void *k, const void *vt, void *o, float *lse,
+                 int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                 float scale, int is_causal, void *stream);
+
+/* attn_fwd_fp8_validate -- the checks of attn_fwd_fp8 without a launch. */
+int attn_fwd_fp8_validate(const void *q, const void *k, const void *vt,
+                          const void *o, const float *lse, int64_t B,
+                          int64_t H, int64_t M, int64_t N, int64_t D,
+                          float scale, int is_causal);
+
 /* attn_fwd_dv -- attn_fwd with a value head dim Dv of its own ("Blackwell
  * Attention Example", attention kernel: v may be [.., N, Dv]):
  *

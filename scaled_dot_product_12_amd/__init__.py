@@ -47,7 +47,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
            "attn_fwd_select_path", "attn_status_string", "attn_bwd",
            "attn_bwd_validate", "axial_pass", "axial_pass_validate", "axial_block",
            "attn_fwd_dv", "attn_fwd_dv_validate", "axial_pass_split",
-           "attn_bwd_noalloc")
+           "attn_bwd_noalloc", "attn_fwd_fp8", "attn_fwd_fp8_validate")
 
 _lib = None
 
@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = cint
         L.attn_bwd_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, cint, cint, vp]
         L.attn_bwd_noalloc.restype = cint
+        L.attn_fwd_fp8.argtypes = [vp] * 5 + [i64] * 5 + [ctypes.c_float, cint, vp]
+        L.attn_fwd_fp8.restype = cint
+        L.attn_fwd_fp8_validate.argtypes = [vp] * 5 + [i64] * 5 + [ctypes.c_float, cint]
+        L.attn_fwd_fp8_validate.restype = cint
         L.attn_bwd_validate.argtypes = [vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint]
         L.attn_bwd_validate.restype = cint
         L.attn_fwd_dv.argtypes = [vp] * 5 + [i64] * 6 + [ctypes.c_float, cint, cint, vp]
@@ -200,6 +204,54 @@ def attn_fwd(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
                                      int(path), stream)
     if st != MI355_ATTN_OK:
         raise RuntimeError(f"attn_fwd failed: {attn_status_string(st)} ({st})")
+    return o, lse
+
+
+def attn_fwd_fp8_validate(q, k, vt, o, lse, B, H, M, N, D, scale, is_causal) -> int:
+    """Status attn_fwd_fp8 would return; pointers are ints (addresses) or None."""
+    return lib().attn_fwd_fp8_validate(q, k, vt, o, lse, B, H, M, N, D, float(scale),
+                                       int(is_causal))
+
+
+def attn_fwd_fp8(q, k, vt, is_causal: bool = False, scale: Optional[float] = None,
+                 out: Optional[Tuple] = None):
+    """(O, L) of attention on fp8 inputs: q [B,H,M,D] and k [B,H,N,D] as
+    torch.float8_e4m3fn, vt = V transposed, [B,H,D,N] float8_e4m3fn (as the
+    Blackwell example takes fp8 values). O is bf16 [B,H,M,D], L fp32 [B,H,M].
+    D in {64, 128}, N a multiple of 16. Asynchronous on torch's current stream.
+    """
+    import torch
+    f8 = torch.float8_e4m3fn
+    for name, t in (("q", q), ("k", k), ("vt", vt)):
+        if t.device.type != "cuda" or t.dtype != f8 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D float8_e4m3fn GPU tensor")
+    if not (q.device == k.device == vt.device):
+        raise ValueError("q, k, vt must be on one device")
+    B, H, M, D = q.shape
+    N = k.shape[2]
+    if tuple(k.shape) != (B, H, N, D) or tuple(vt.shape) != (B, H, D, N):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
+                         f"vt {tuple(vt.shape)} (vt is [B, H, D, N])")
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        o = torch.empty((B, H, M, D), dtype=torch.bfloat16, device=q.device)
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if (tuple(o.shape) != (B, H, M, D) or o.dtype != torch.bfloat16
+                or not o.is_contiguous() or o.device != q.device):
+            raise ValueError("out[0] must be a contiguous bf16 [B, H, M, D] tensor on q's device")
+        if (tuple(lse.shape) != (B, H, M) or lse.dtype != torch.float32
+                or not lse.is_contiguous() or lse.device != q.device):
+            raise ValueError("out[1] must be a contiguous fp32 [B, H, M] tensor on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = lib().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, H, M, N, D, float(scale),
+                                int(bool(is_causal)), stream)
+    if st != MI355_ATTN_OK:
+        raise RuntimeError(f"attn_fwd_fp8 failed: {attn_status_string(st)} ({st})")
     return o, lse
 
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 
 SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
            "attn_fwd_small.hip", "attn_bwd_bf16.hip", "axial_api.cpp",
-           "axial_block.hip", "attn_noalloc.hip"]
+           "axial_block.hip", "attn_noalloc.hip", "attn_fwd_fp8.hip"]
 
 
 def hipcc() -> str:

@@ -135,6 +135,40 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o,
   return MI355_ATTN_OK;
 }
 
+// attn_fwd_fp8: e4m3 q, k and transposed v; bf16 o; fp32 lse.
+int validate_fp8(const void* q, const void* k, const void* vt, const void* o, const float* lse,
+                 int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,
+                 int is_causal) {
+  if (B < 0 || H < 0 || M < 0 || D < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (is_causal != 0 && is_causal != 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MI355_ATTN_ERR_INVALID_ARG;
+  int64_t BH, rows;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, M, &rows)) return MI355_ATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return MI355_ATTN_OK;
+  if (N < 1) return MI355_ATTN_ERR_INVALID_ARG;
+  if (!q || !k || !vt || !o || !lse) return MI355_ATTN_ERR_INVALID_ARG;
+  if ((D != 64 && D != 128) || N % 16 != 0) return MI355_ATTN_ERR_UNSUPPORTED;
+  int64_t md, nd, q_bytes, kv_bytes, o_bytes, lse_bytes;
+  if (!mul_ok(M, D, &md) || !mul_ok(N, D, &nd) || md > kIntMax || nd > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (!mul_ok(rows, D, &q_bytes) || !mul_ok(BH, nd, &kv_bytes) || !mul_ok(q_bytes, 2, &o_bytes) ||
+      !mul_ok(rows, 4, &lse_bytes))
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  const int64_t tile = mi355::fp8_tile_rows();
+  int64_t grid;
+  if (!mul_ok((M + tile - 1) / tile, BH, &grid) || grid > kIntMax)
+    return MI355_ATTN_ERR_UNSUPPORTED;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)vt | (uintptr_t)o) & 15u)
+    return MI355_ATTN_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3u) return MI355_ATTN_ERR_MISALIGNED;
+  if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, k, kv_bytes) ||
+      overlap(o, o_bytes, vt, kv_bytes) || overlap(lse, lse_bytes, q, q_bytes) ||
+      overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, vt, kv_bytes) ||
+      overlap(lse, lse_bytes, o, o_bytes))
+    return MI355_ATTN_ERR_INVALID_ARG;
+  return MI355_ATTN_OK;
+}
+
 int select_path(int64_t M, int64_t N, int64_t D) {
   return small_fits(M, N, D) ? MI355_ATTN_PATH_SMALL : MI355_ATTN_PATH_MAIN;
 }
@@ -357,6 +391,34 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   const hipError_t err =
       dtype == MI355_ATTN_FP16 ? mi355::launch_bwd_f16(a) : mi355::launch_bwd_bf16(a);
   return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
+}
+
+int attn_fwd_fp8_validate(const void* q, const void* k, const void* vt, const void* o,
+                          const float* lse, int64_t B, int64_t H, int64_t M, int64_t N,
+                          int64_t D, float scale, int is_causal) {
+  return validate_fp8(q, k, vt, o, lse, B, H, M, N, D, scale, is_causal);
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int64_t B,
+                 int64_t H, int64_t M, int64_t N, int64_t D, float scale, int is_causal,
+                 void* stream) {
+  const int st = validate_fp8(q, k, vt, o, lse, B, H, M, N, D, scale, is_causal);
+  if (st != MI355_ATTN_OK) return st;
+  if (B * H * M == 0) return MI355_ATTN_OK;
+  mi355::Fp8LaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.vt = vt;
+  a.o = o;
+  a.lse = lse;
+  a.BH = B * H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.causal = is_causal != 0;
+  a.stream = (hipStream_t)stream;
+  return mi355::launch_fp8(a) == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 
 const char* attn_status_string(int status) {

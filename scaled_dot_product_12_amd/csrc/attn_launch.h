@@ -35,6 +35,23 @@ hipError_t launch_small(const LaunchArgs& a, int et);
 int main_bf16_tile_rows();
 int main_f32_tile_rows();
 
+// fp8 (e4m3) forward: q [BH, M, D], k [BH, N, D], vt [BH, D, N] (V
+// transposed), o bf16 [BH, M, D], lse fp32; D in {64, 128}, N % 16 == 0.
+struct Fp8LaunchArgs {
+  const void* q;
+  const void* k;
+  const void* vt;
+  void* o;
+  float* lse;
+  int64_t BH;
+  int64_t M, N, D;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+hipError_t launch_fp8(const Fp8LaunchArgs& a);
+int fp8_tile_rows();
+
 struct BwdLaunchArgs {
   const void* q;
   const void* k;

@@ -5,8 +5,8 @@ them. Both the HIP path's tests/benchmark and the CPU oracle are fed from here.
 
 Recipe (every workload): ``g = torch.Generator("cpu").manual_seed(seed)``, then
 Q, K, V in that order, each ``torch.randn(shape, dtype=float32, generator=g)``.
-bf16 (fp16) workloads round those fp32 draws with ``.to(torch.bfloat16)``
-(``.to(torch.float16)``), round-to-nearest-even. The upstream gradient dO of a backward problem is
+bf16 (fp16, fp8) workloads round those fp32 draws with ``.to(torch.bfloat16)``
+(``.to(torch.float16)``, ``.to(torch.float8_e4m3fn)``), round-to-nearest-even. The upstream gradient dO of a backward problem is
 drawn the same way from its own generator, seeded with ``seed + DOUT_SEED_OFFSET``
 (so Q, K, V are the same draws as the forward problem's). Shapes follow the
 pages' workloads:
@@ -38,7 +38,7 @@ class Workload:
     M: int
     N: int
     D: int
-    dtype: str            # "fp32", "bf16" or "fp16"
+    dtype: str            # "fp32", "bf16", "fp16" or "fp8" (e4m3 inputs, bf16 output)
     causal: bool
     seed: int
     axial: str = ""       # "" or "row" / "col" / "both" for the axial passes
@@ -56,9 +56,12 @@ class Workload:
         return f / 2 if self.causal else f
 
     def algorithmic_bytes(self) -> int:
-        """Read Q, K, V once; write O once (input dtype) and L once (fp32)."""
-        es = 4 if self.dtype == "fp32" else 2
-        return (es * self.B * self.H * (2 * self.M * self.D + 2 * self.N * self.D)
+        """Read Q, K, V once; write O once (the input dtype; bf16 for fp8
+        inputs) and L once (fp32)."""
+        es_in = {"fp32": 4, "bf16": 2, "fp16": 2, "fp8": 1}[self.dtype]
+        es_out = 2 if self.dtype == "fp8" else es_in
+        return (self.B * self.H * (es_in * (self.M + 2 * self.N) * self.D
+                                   + es_out * self.M * self.D)
                 + 4 * self.B * self.H * self.M)
 
     def describe(self) -> str:
@@ -99,9 +102,15 @@ WORKLOADS: Dict[str, Workload] = {
     # describes its test as float16): the same draws as c4, rounded to fp16.
     "c4h": Workload("c4h", 4, 16, 4096, 4096, 128, "fp16", False, 4,
                     note="long-sequence fp16"),
+    # The long-sequence shape with fp8 (e4m3) inputs and P rounded to fp8 for
+    # the second product (the Blackwell example casts P to the value dtype):
+    # c4's draws rounded to e4m3; V is handed to the kernel transposed.
+    "c4f8": Workload("c4f8", 4, 16, 4096, 4096, 128, "fp8", False, 4,
+                     note="long-sequence fp8 e4m3"),
 }
 
-_DT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
+_DT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16,
+       "fp8": torch.float8_e4m3fn}
 
 
 def make_qkv(B: int, H: int, M: int, N: int, D: int, dtype: str = "fp32",

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
         ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
          "attn_status_string", "attn_bwd", "attn_bwd_validate", "axial_pass",
          "axial_pass_validate", "axial_block", "attn_fwd_dv", "attn_fwd_dv_validate",
-         "axial_pass_split", "attn_bwd_noalloc"])
+         "axial_pass_split", "attn_bwd_noalloc", "attn_fwd_fp8", "attn_fwd_fp8_validate"])
 
 
 def test_library_exports_every_declared_symbol(hip_lib):
@@ -295,3 +295,29 @@ def test_bwd_noalloc_checks_before_any_hip_call(hip_lib):
     assert call(1, 1, 5, 5, dq=q) == INVALID     # output overlaps an input
     # the capacity check comes after attn_bwd's own checks
     assert call(1, 1, cap + 1, 64, dq=None) == INVALID
+
+
+def test_fp8_validation_before_any_hip_call(hip_lib):
+    """attn_fwd_fp8_validate: e4m3 q/k, transposed e4m3 v, bf16 o, fp32 lse;
+    D in {64, 128}, N a multiple of 16; the usual pointer, alignment and
+    overlap rules (stand-in addresses, never dereferenced)."""
+    sz = 1 << 36
+    q, k, vt, o, lse = ((i + 1) * sz for i in range(5))
+
+    def v(B=4, H=16, M=4096, N=4096, D=128, scale=0.088, causal=0, **kw):
+        p = dict(q=q, k=k, vt=vt, o=o, lse=lse)
+        p.update(kw)
+        return hip_lib.attn_fwd_fp8_validate(p["q"], p["k"], p["vt"], p["o"], p["lse"], B, H, M,
+                                             N, D, scale, causal)
+
+    assert v() == OK
+    assert v(D=64, N=16, M=1) == OK
+    assert v(B=0) == OK and v(M=0) == OK            # nothing to do
+    assert v(D=32) == UNSUPPORTED and v(D=96) == UNSUPPORTED
+    assert v(N=4000 + 8) == UNSUPPORTED             # N % 16 != 0
+    assert v(N=0) == INVALID
+    assert v(q=None) == INVALID and v(vt=None) == INVALID and v(lse=None) == INVALID
+    assert v(scale=float("inf")) == INVALID and v(causal=2) == INVALID
+    assert v(o=o + 8) == MISALIGNED and v(vt=vt + 4) == MISALIGNED and v(lse=lse + 2) == MISALIGNED
+    assert v(o=q) == INVALID                          # output over an input
+    assert v(lse=o + 1024) == INVALID                 # lse inside o
