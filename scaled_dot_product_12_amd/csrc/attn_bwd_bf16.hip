@@ -125,6 +125,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* head
   return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)row0 * D), (short)0,
                                            (int)bytes, kBufferRsrcWord3);
 }
+// The same descriptor as four words, for the loads into LDS (lds_dma16).
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+template <int D>
+__device__ __forceinline__ i32x4_t rows_desc(const uint16_t* head, int row0, int rows) {
+  const int left = rows - row0;
+  const uint32_t bytes = left > 0 ? (uint32_t)left * (uint32_t)(2 * D) : 0u;
+  const uint64_t base = (uint64_t)(head + (size_t)row0 * D);
+  return (i32x4_t){(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)bytes,
+                   kBufferRsrcWord3};
+}
 
 // Per-lane LDS offsets of the two fragment kinds read from a Tile.
 template <int D>
@@ -189,10 +199,20 @@ __device__ __forceinline__ void load_b_rows(const uint16_t* head, int x, int row
 typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from a buffer straight into LDS: lane l writes
-// lds_wave_base + 16*l (lds_wave_base must be wave-uniform).
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_wave_base,
-                                          int voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voffset, 0, 0, 0);
+// lds_wave_base + 16*l (lds_wave_base must be wave-uniform). Written as
+// inline asm: the compiler, which cannot tell the two ring slots apart, would
+// otherwise make every later LDS read wait for these loads, i.e. wait in the
+// middle of each tile for the next tile's data. The kernels order them
+// themselves: a slot is loaded only after the barrier that ends its last
+// reads, and every load is waited for (wait_vmem) before the barrier that
+// publishes its slot. The instruction has no result register; its address
+// operands are read when it issues.
+__device__ __forceinline__ void lds_dma16(i32x4_t desc, unsigned char* lds_wave_base, int voffset) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(desc)
+               : "m0");
 }
 
 // Wait for this wave's outstanding vector-memory operations (including
@@ -260,8 +280,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
   // K and V tiles go from HBM straight into LDS (buffer loads with the lds
   // flag; lane l of a wave writes the wave's base + 16 l).
   auto load = [&](int j, int buf) {
-    const auto rk = rows_rsrc<D>(kh, j * BN, N);
-    const auto rv = rows_rsrc<D>(vh, j * BN, N);
+    const i32x4_t rk = rows_desc<D>(kh, j * BN, N);
+    const i32x4_t rv = rows_desc<D>(vh, j * BN, N);
 #pragma unroll
     for (int u = 0; u < Stager<D, NT>::CPT; ++u) {
       const int wbase = (wave * 64 + u * NT) * 16;  // wave-uniform
@@ -439,14 +459,14 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
   FragAddr<D> fa;
   fa.init(lane);
   constexpr int CPT = Stager<D, NT>::CPT;
-  float stat = 0.0f;  // threads 0..63: log2e*L of a row; 64..127: delta
+  float stat = 0.0f;  // threads 0..63: L of a row; 64..127: delta (as loaded)
   // Q and dO tiles go from HBM straight into LDS (buffer loads with the lds
   // flag: lane l of a wave writes 16 bytes at the wave's base + 16 l, which
   // is the staging order ch = tid + u*NT), so they need no registers; the
   // per-row statistics pass through one register.
   auto load = [&](int j, int buf) {
-    const auto rq = rows_rsrc<D>(qh, j * BQ, M);
-    const auto rg = rows_rsrc<D>(gh, j * BQ, M);
+    const i32x4_t rq = rows_desc<D>(qh, j * BQ, M);
+    const i32x4_t rg = rows_desc<D>(gh, j * BQ, M);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int wbase = (wave * 64 + u * NT) * 16;  // wave-uniform
@@ -459,16 +479,20 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
       const int r = j * BQ + lane;
       const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(wave == 0 ? lh : dh), (short)0,
                                                         M * 4, kBufferRsrcWord3);
-      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, r * 4, 0, 0));
-      // Rows past the end: P = exp2(-inf) = 0 and delta = 0.
-      stat = wave == 0 ? (r < M ? x * kLog2e : INFINITY) : x;
+      // used only in store(), after the tile's products, so that the wait
+      // for it (which also waits for the tile loads) stays there
+      stat = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, r * 4, 0, 0));
     }
   };
   // Make this wave's tile loads and its statistic visible to the workgroup
   // (the caller's barrier follows).
-  auto store = [&](int buf) {
-    if (wave < 2) ((float*)(smem + STAT_OFF))[buf * 2 * BQ + tid] = stat;
+  auto store = [&](int buf, int j) {
     wait_vmem();
+    if (wave < 2) {
+      // Rows past the end: P = exp2(-inf) = 0 and delta = 0.
+      const float x = wave == 0 ? (j * BQ + lane < M ? stat * kLog2e : INFINITY) : stat;
+      ((float*)(smem + STAT_OFF))[buf * 2 * BQ + tid] = x;
+    }
   };
 
   // K^T as the B operand (lane's key row) in registers; V rows
@@ -517,7 +541,10 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
       // chunk i is S step i/2 (even: Q rows, K^T) or dP step i/2 (odd: dO
       // rows, V^T)
       {
-        constexpr int PF = 2, NA = 2 * QSTEPS;
+        // (one chunk ahead at D = 128: two would exceed the register budget,
+        // and the spill reloads inside the loop would each wait for the next
+        // tile's loads)
+        constexpr int PF = D == 128 ? 1 : 2, NA = 2 * QSTEPS;
         bf16x8_t fa_[PF + 1], fb_[PF + 1];
         auto rd = [&](int i, bf16x8_t& x, bf16x8_t& y) {
           x = fa.row_frag((i & 1) ? gt : qt, qb, i >> 1, g);
@@ -589,7 +616,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
 
   if (t_beg < t_end) {
     load(t_beg, 0);
-    store(0);
+    store(0, t_beg);
   }
   __syncthreads();
   for (int j = t_beg; j < t_end; ++j) {
@@ -602,7 +629,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
     // Causal: one body with a tile-uniform mask flag (a second inlined copy
     // of the body would not fit the register budget).
     tile_body(qt, gt, lt, q0, CAUSAL && q0 < kw0 + 31);
-    if (j + 1 < t_end) store(buf ^ 1);
+    if (j + 1 < t_end) store(buf ^ 1, j + 1);
     __syncthreads();
   }
 
