@@ -99,6 +99,11 @@ struct Stager {
   static constexpr int CPT = (T::CHUNKS + NT - 1) / NT;
   int src[CPT];  // byte offset of the source chunk from the tile's first row
   int dst[CPT];  // byte offset in the LDS tile (-1: no chunk for this thread)
+  // Chunk u lies NT / CPR rows (a multiple of 32) below chunk 0 with the same
+  // position: perm and swz act on the low five row bits only, so its source
+  // is chunk 0's plus u * SRC_STEP bytes.
+  static constexpr int SRC_STEP = (NT / T::CPR) * T::ROWB;
+  static_assert(CPT == 1 || (NT / T::CPR) % 32 == 0, "chunk offsets are chunk 0's plus a constant");
   __device__ void init(int tid) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
@@ -198,6 +203,10 @@ __device__ __forceinline__ void load_b_rows(const uint16_t* head, int x, int row
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// An empty volatile asm statement: a branch body containing it is not
+// if-converted into selects executed on every tile.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
 // 16 bytes per lane from a buffer straight into LDS: lane l writes
 // lds_wave_base + 16*l (lds_wave_base must be wave-uniform). Written as
 // inline asm: the compiler, which cannot tell the two ring slots apart, would
@@ -206,12 +215,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // themselves: a slot is loaded only after the barrier that ends its last
 // reads, and every load is waited for (wait_vmem) before the barrier that
 // publishes its slot. The instruction has no result register; its address
-// operands are read when it issues.
-__device__ __forceinline__ void lds_dma16(i32x4_t desc, unsigned char* lds_wave_base, int voffset) {
+// operands are read when it issues. soffset (wave-uniform) is added to the
+// per-lane voffset.
+__device__ __forceinline__ void lds_dma16(i32x4_t desc, unsigned char* lds_wave_base, int voffset,
+                                          int soffset) {
   const uint32_t lds = (uint32_t)(uintptr_t)(lds_void*)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds), "v"(voffset), "s"(desc)
+               : "s"(lds), "v"(voffset), "s"(desc), "s"(soffset)
                : "m0");
 }
 
@@ -286,8 +297,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
     for (int u = 0; u < Stager<D, NT>::CPT; ++u) {
       const int wbase = (wave * 64 + u * NT) * 16;  // wave-uniform
       if (wbase < T::BYTES) {
-        lds_dma16(rk, smem + buf * T::BYTES + wbase, st.src[u]);
-        lds_dma16(rv, smem + (2 + buf) * T::BYTES + wbase, st.src[u]);
+        lds_dma16(rk, smem + buf * T::BYTES + wbase, st.src[0], u * Stager<D, NT>::SRC_STEP);
+        lds_dma16(rv, smem + (2 + buf) * T::BYTES + wbase, st.src[0], u * Stager<D, NT>::SRC_STEP);
       }
     }
   };
@@ -366,6 +377,22 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
     // P = 0. Rounded to bf16: the B operand of dQ^T += K^T dS^T.
     const int key0 = j * BN;
     const bool masked = (key0 + BN > N) || (CAUSAL && key0 + BN - 1 > qw0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -l2));
+    if (masked) {
+      // only tiles that cross the diagonal or the last key: a real branch
+      // (not per-element selects on every tile)
+      keep_branch();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + g * 16 + i;
+          if (key >= N || (CAUSAL && key > qi)) s[kb][i] = 0.0f;
+        }
+    }
     u32x4_t ds[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -374,12 +401,7 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i0 = t * 8 + 2 * e;
-          float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i0], c, -l2));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + 1], c, -l2));
-          const int key = key0 + kb * 32 + g * 16 + i0;
-          p0 = masked && (key >= N || (CAUSAL && key > qi)) ? 0.0f : p0;
-          p1 = masked && (key + 1 >= N || (CAUSAL && key + 1 > qi)) ? 0.0f : p1;
-          ds[kb][t][e] = H::pack(p0 * (dp[kb][i0] - dl), p1 * (dp[kb][i0 + 1] - dl));
+          ds[kb][t][e] = H::pack(s[kb][i0] * (dp[kb][i0] - dl), s[kb][i0 + 1] * (dp[kb][i0 + 1] - dl));
         }
 
     // dQ^T += K^T dS^T over the tile's four 16-key steps (chunk i: d block
@@ -471,8 +493,8 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
     for (int u = 0; u < CPT; ++u) {
       const int wbase = (wave * 64 + u * NT) * 16;  // wave-uniform
       if (wbase < T::BYTES) {
-        lds_dma16(rq, smem + buf * T::BYTES + wbase, st.src[u]);
-        lds_dma16(rg, smem + (2 + buf) * T::BYTES + wbase, st.src[u]);
+        lds_dma16(rq, smem + buf * T::BYTES + wbase, st.src[0], u * Stager<D, NT>::SRC_STEP);
+        lds_dma16(rg, smem + (2 + buf) * T::BYTES + wbase, st.src[0], u * Stager<D, NT>::SRC_STEP);
       }
     }
     if (wave < 2) {  // wave 0: log2e*L, wave 1: delta of the tile's rows
@@ -567,6 +589,9 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
         }
       }
       const int qr0 = qb * 32 + 16 * g;  // lane's queries q0 + qr0 + r, r < 16
+      // first masked register index of this lane on a diagonal tile: query
+      // q0 + qr0 + i sees key kj iff i >= kj - q0 - qr0
+      const int vis0 = kj - q0 - qr0;
       u32x4_t pb[2], dsb[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -580,9 +605,10 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
             float p0 = __builtin_amdgcn_exp2f(fmaf(s[i0], c, -la[2 * e2]));
             float p1 = __builtin_amdgcn_exp2f(fmaf(s[i0 + 1], c, -la[2 * e2 + 1]));
             if (mask) {
-              const int qq = q0 + qr0 + i0;
-              p0 = kj > qq ? 0.0f : p0;
-              p1 = kj > qq + 1 ? 0.0f : p1;
+              // diagonal tiles only: a real branch, not selects on every tile
+              keep_branch();
+              p0 = i0 < vis0 ? 0.0f : p0;
+              p1 = i0 + 1 < vis0 ? 0.0f : p1;
             }
             pb[t][e] = H::pack(p0, p1);
             dsb[t][e] = H::pack(p0 * (dp[i0] - da[2 * e2]), p1 * (dp[i0 + 1] - da[2 * e2 + 1]));
