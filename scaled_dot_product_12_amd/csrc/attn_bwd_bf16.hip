@@ -20,13 +20,12 @@
 //    second kernel. Per tile: S^T = K Q^T and dP^T = V dO^T (K, V rows from
 //    LDS, Q^T, dO^T in registers), P^T and dS^T in registers, then
 //    dQ^T += K^T dS^T with K^T read from LDS through ds_read_b64_tr_b16.
-//  * attn_bwd_dkdv_kernel: one workgroup = 4 waves = 128 key rows, one wave
-//    per SIMD (its dK^T, dV^T accumulators and K^T, V^T operands need ~360
-//    registers); loops over query tiles of 64 rows, staged straight from HBM
-//    into LDS. Per tile: S = Q K^T, dP = dO V^T (Q, dO rows from LDS, K^T, V^T
-//    in registers) for both 32-query halves, then per half P and dS, then
-//    dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed from
-//    LDS.
+//  * attn_bwd_dkdv_kernel: one workgroup = 8 waves = 256 key rows (two
+//    waves per SIMD); loops over query tiles of 64 rows. Per 32-query half:
+//    S = Q K^T and dP = dO V^T (Q, dO rows from LDS, K^T in registers, V^T
+//    from the workgroup's V rows kept in LDS for the whole kernel), P and dS,
+//    then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed
+//    from LDS.
 //  * For D <= 64 both kernels use 4-wave workgroups (128 rows), three per CU,
 //    so that three waves share each SIMD.
 //  * All products are v_mfma_f32_32x32x16_bf16. Every staged tile is stored
@@ -34,8 +33,12 @@
 //    are 16 consecutive rows of the tile: rounded to bf16 those registers are
 //    directly the B operand of the next product. Tiles are XOR-swizzled at
 //    16-byte granularity.
-//  * Tiles stream HBM -> VGPRs -> LDS through bounded buffer loads (rows past
-//    the head read as zeros), double-buffered, one barrier per tile.
+//  * Tiles go from HBM straight into LDS (buffer loads with the lds flag,
+//    bounded: rows past the head read as zeros), double-buffered, one barrier
+//    per tile. Nothing in the loops waits for the next tile's loads before
+//    the tile's last product: the loads are issued from inline asm (see
+//    lds_dma16), masks are branches, and no spill reload comes before the
+//    tile's last product.
 
 #include "attn_device.h"
 #include "attn_launch.h"
