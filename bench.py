@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--axial-only", action="store_true",
                     help="only time the fused axial block and its passes (for profiling)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time attn_bwd on --workload (16-bit workloads; for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -465,6 +467,13 @@ def main():
 
     if a.axial_only:
         print(json.dumps(measure_axial_block(a.steps)), flush=True)
+        return
+    if a.backward_only:
+        w = WORKLOADS[a.workload]
+        ms, tf, st = measure_bwd(w, a.steps, a.warmup)
+        print(json.dumps({"backward": w.describe(), "us_per_call": round(ms * 1e3, 3),
+                          "tflops": round(tf, 3), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "repeat": st}), flush=True)
         return
     w = WORKLOADS[a.workload]
     print(f"[bench] headline {w.describe()}", file=sys.stderr, flush=True)
