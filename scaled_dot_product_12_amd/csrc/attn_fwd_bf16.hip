@@ -420,7 +420,19 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D > DV ? D : DV)) vo
   };
 
   // Second half, as NF_PV fenced chunks: the V^T fragment reads VPF chunks
-  // ahead, one O MFMA each and, with a next tile, the loads of V(j+1).
+  // ahead, one O MFMA each and, with a next tile, the loads of V(j+1) (first
+  // chunks). With 8 waves the LDS writes of K(j+2) (from the middle) and
+  // V(j+1) (last quarter) go between these products too, rather than all at
+  // the end of a half, where they hold up the barrier (about 1% at D = 128;
+  // the 4-wave kernels keep them at the ends: their register budget is
+  // smaller). Both slots are free: their last reads ended before the
+  // previous barrier.
+  constexpr bool STG_IN_B = WAVES == 8;
+  constexpr int KST0 = NF_PV / 2, KSTEP = NF_PV / (2 * CPT) > 0 ? NF_PV / (2 * CPT) : 1;
+  constexpr int VST0 = 3 * NF_PV / 4, VSTEP = NF_PV / (4 * VCPT) > 0 ? NF_PV / (4 * VCPT) : 1;
+  static_assert(KST0 + (CPT - 1) * KSTEP < NF_PV && VST0 + (VCPT - 1) * VSTEP < NF_PV &&
+                    VST0 >= VCPT,
+                "staging writes fit the chunks, after the V loads");
   auto region_b = [&](int j, const u32x4_t (*p)[2], bool has_next) __attribute__((always_inline)) {
     const unsigned char* vb_base = smem + C::V_OFF + (j & 1) * VTILEB;
     const auto rv = tile_rsrc_v(j + 1);
@@ -432,6 +444,14 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D > DV ? D : DV)) vo
       if (i + VPF < NF_PV) fr[(i + VPF) % (VPF + 1)] = v_frag(vb_base, i + VPF);
       if (has_next && i < VCPT)
         vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_src0 + v_src_off(i), 0, 0);
+      if (STG_IN_B && has_next && i >= KST0 && (i - KST0) % KSTEP == 0 && (i - KST0) / KSTEP < CPT) {
+        const int u = (i - KST0) / KSTEP;
+        *(u32x4_t*)(smem + ((j + 2) % C::KBUF) * C::KTILEB + kdst0 + kdst_off(u)) = kst[u];
+      }
+      if (STG_IN_B && has_next && i >= VST0 && (i - VST0) % VSTEP == 0 && (i - VST0) / VSTEP < VCPT) {
+        const int u = (i - VST0) / VSTEP;
+        *(u32x4_t*)(smem + C::V_OFF + ((j + 1) & 1) * VTILEB + dst0 + dst_off(u)) = vst[u];
+      }
       const int b = i % DBLK, kt = i / DBLK;
       acc[b] = H::mma(__builtin_bit_cast(u32x4_t, fr[i % (VPF + 1)]), p[kt >> 1][kt & 1], acc[b]);
       __builtin_amdgcn_sched_barrier(0);
@@ -452,7 +472,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D > DV ? D : DV)) vo
     float rs;
     if (has_next) {
       rs = region_a(j, sc, sn, p);
-      store_k((j + 2) % C::KBUF);
+      if constexpr (!STG_IN_B) store_k((j + 2) % C::KBUF);
     } else {
       rs = tile_exp(sc[0], p[0]) + tile_exp(sc[1], p[1]);
     }
@@ -471,7 +491,7 @@ __global__ __launch_bounds__(WAVES * 64, bf16_blocks_per_cu(D > DV ? D : DV)) vo
     l_run += rs;
     region_b(j, p, has_next);
     if (has_next) {
-      store_v((j + 1) & 1);
+      if constexpr (!STG_IN_B) store_v((j + 1) & 1);
       scale_tile(sn);
       if (needs_mask(j + 1)) {
         keep_branch();
