@@ -303,7 +303,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8_kernel(
     return xm;
   };
   // Second half: O^T += V^T P^T (DBLK MFMAs) and the row-sum MFMA; the
-  // loads of V(j+1) go out at the start.
+  // loads of V(j+1) go out at the start, and K(j+2) is written to its ring
+  // slot beside the first product (not at the end of the first half, where
+  // the write waits for its loads in front of the exact-path check).
   auto region_b = [&](int j, const i32x8_t& p, bool has_next) __attribute__((always_inline)) {
     const int buf = j & 1;
     if (has_next) load_v(j + 1);
@@ -312,6 +314,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8_kernel(
     for (int b = 0; b < DBLK; ++b) {
       const i32x8_t cur = fr;
       if (b + 1 < DBLK) fr = v_frag(buf, b + 1);
+      if (has_next && b == 0) store_k((j + 2) % C::KBUF);
       acc[b] = mma_fp8(cur, p, acc[b]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -323,7 +326,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8_kernel(
     float xm;
     if (has_next) {
       xm = region_a(j, sc, sn, p);
-      store_k((j + 2) % C::KBUF);
     } else {
       xm = tile_exp(sc, p);
     }
