@@ -244,8 +244,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_fp8_kernel(
     const float a0 = fmaf(x0, cc_scale, -m_sub), a1 = fmaf(x1, cc_scale, -m_sub);
     const float a2 = fmaf(x2, cc_scale, -m_sub), a3 = fmaf(x3, cc_scale, -m_sub);
     xm = __builtin_fmaxf(xm, __builtin_fmaxf(__builtin_fmaxf(a0, a1), __builtin_fmaxf(a2, a3)));
+    // the first conversion fills bytes 0-1 and keeps bytes 2-3 of its third
+    // operand, which the second conversion then overwrites: any register will
+    // do there (a dead one costs no move, where a zero costs one per dword)
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(a0), __builtin_amdgcn_exp2f(a1),
-                                           0, false);
+                                           __float_as_int(a0), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(a2), __builtin_amdgcn_exp2f(a3), w,
                                        true);
     return w;
