@@ -242,9 +242,12 @@ def bwd_flops(w) -> float:
     return f / 2 if w.causal else f
 
 
-def measure_bwd(w, steps, warmup):
-    """Average time of one attn_bwd call (dQ kernel + dK/dV kernel) on the
-    workload's tensors, with the forward's O and L and a seeded dO."""
+def measure_bwd(w, steps, warmup, one_pass=True):
+    """Average time of one attn_bwd call on the workload's tensors, with the
+    forward's O and L and a seeded dO: the one-pass path (delta kernel + fused
+    kernel, work area allocated beforehand) where it applies and one_pass is
+    set, else the two kernels (dQ kernel + dK/dV kernel). Returns the path
+    taken too."""
     import torch
     import scaled_dot_product_12_amd as attn
     from scaled_dot_product_12_amd.inputs import make_dout
@@ -253,12 +256,16 @@ def measure_bwd(w, steps, warmup):
     g = make_dout(w.B, w.H, w.M, w.D, w.dtype, w.seed).to(q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    code = attn.MI355_ATTN_FP16 if w.dtype == "fp16" else attn.MI355_ATTN_BF16
+    need = attn.attn_bwd_work_bytes(w.B, w.H, w.M, w.N, w.D, w.causal, code) if one_pass else 0
+    work = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
 
     def fn():
         attn.attn_bwd(q, k, v, o, lse, g, is_causal=w.causal, scale=w.scale,
-                      out=(dq, dk, dv), delta=delta)
+                      out=(dq, dk, dv), delta=delta, one_pass=one_pass, work=work)
     ms, _, st = time_launches(fn, steps, warmup)
-    return ms, bwd_flops(w) / (ms * 1e-3) / 1e12, st
+    path = "one pass (delta + fused kernel)" if need else "two kernels (dQ, dK/dV)"
+    return ms, bwd_flops(w) / (ms * 1e-3) / 1e12, st, path
 
 
 def measure(w, steps, warmup, graph):
@@ -470,10 +477,12 @@ def main():
         return
     if a.backward_only:
         w = WORKLOADS[a.workload]
-        ms, tf, st = measure_bwd(w, a.steps, a.warmup)
-        print(json.dumps({"backward": w.describe(), "us_per_call": round(ms * 1e3, 3),
-                          "tflops": round(tf, 3), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                          "repeat": st}), flush=True)
+        for one_pass in (True, False):
+            ms, tf, st, path = measure_bwd(w, a.steps, a.warmup, one_pass)
+            print(json.dumps({"backward": w.describe(), "path": path,
+                              "us_per_call": round(ms * 1e3, 3), "tflops": round(tf, 3),
+                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "repeat": st}), flush=True)
         return
     w = WORKLOADS[a.workload]
     print(f"[bench] headline {w.describe()}", file=sys.stderr, flush=True)
@@ -534,14 +543,24 @@ def main():
             x = WORKLOADS[name]
             steps = max(5, min(30, int(4e12 / bwd_flops(x))))
             print(f"[bench] backward {x.describe()}", file=sys.stderr, flush=True)
-            bms, btf, bst = measure_bwd(x, steps, 3)
+            bms, btf, bst, path = measure_bwd(x, steps, 3)
             torch.cuda.empty_cache()
             extra["bwd_" + name] = {
-                "workload": "backward (dQ, dK, dV) " + x.describe(),
+                "workload": "backward (dQ, dK, dV) " + x.describe(), "path": path,
                 "us_per_call": round(bms * 1e3, 3), "tflops": round(btf, 3),
                 "flops_per_call": bwd_flops(x), "frac_compute_peak": round(btf / PEAK_BF16_TFLOPS, 4),
                 "timing": "%d calls" % steps, "repeat": bst,
             }
+            if path.startswith("one pass"):
+                tms, ttf, tst, tpath = measure_bwd(x, steps, 3, one_pass=False)
+                torch.cuda.empty_cache()
+                extra["bwd_" + name + "_two_kernels"] = {
+                    "workload": "backward (dQ, dK, dV) " + x.describe(), "path": tpath,
+                    "us_per_call": round(tms * 1e3, 3), "tflops": round(ttf, 3),
+                    "flops_per_call": bwd_flops(x),
+                    "frac_compute_peak": round(ttf / PEAK_BF16_TFLOPS, 4),
+                    "timing": "%d calls" % steps, "repeat": tst,
+                }
 
     cpu = None
     if not a.no_cpu_baseline:

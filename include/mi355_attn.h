@@ -192,6 +192,56 @@ int attn_bwd_validate(const void *q, const void *k, const void *v,
                       int dtype);
 
 /*
+ * attn_bwd_ws -- attn_bwd with a device work area, which lets it run the
+ * backward in one pass over the keys ("Blackwell Attention Example",
+ * backward kernel section: the key-tile loop that adds each tile's share of
+ * dQ). Here the shares are added in a fixed order (key tile 0, 1, 2, ...)
+ * instead of with atomics, so the results are the same on every run, like
+ * attn_bwd's; S and dP are then formed once per (query, key) pair instead of
+ * twice.
+ *
+ *   work, work_bytes  caller-owned device memory, 256-byte aligned, not
+ *              overlapping any other argument; its prior contents are
+ *              ignored and the call overwrites the first
+ *              attn_bwd_work_bytes(...) bytes.
+ *   all other arguments as for attn_bwd.
+ *
+ * The one-pass path applies to bf16 and fp16 with D = 128, no causal mask,
+ * B*H a multiple of 8 and B*H*M <= 2^30; otherwise, or with work == NULL or
+ * work_bytes below attn_bwd_work_bytes(...), the call is exactly attn_bwd.
+ * Enqueues two kernels on `stream` (delta, then the one-pass kernel). The
+ * dQ, dK and dV it returns are deterministic but need not equal attn_bwd's
+ * bit for bit (dQ is summed in another order).
+ *
+ * Returns what attn_bwd returns, or MISALIGNED (work not 256-byte aligned)
+ * or INVALID_ARG (work overlapping another argument, work_bytes < 0) when
+ * the one-pass path would run.
+ */
+int attn_bwd_ws(const void *q, const void *k, const void *v, const void *o,
+                const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                float *delta, int64_t B, int64_t H, int64_t M, int64_t N,
+                int64_t D, float scale, int is_causal, int dtype, void *work,
+                int64_t work_bytes, void *stream);
+
+/*
+ * attn_bwd_work_bytes -- bytes of work area with which attn_bwd_ws runs its
+ * one-pass path for these sizes (B*H*M*D*4 for the fp32 dQ sums, B*H*M*4 for
+ * L in base 2, and counters), or 0 where that path does not apply. No HIP
+ * call.
+ */
+int64_t attn_bwd_work_bytes(int64_t B, int64_t H, int64_t M, int64_t N,
+                            int64_t D, int is_causal, int dtype);
+
+/*
+ * attn_bwd_work_error_offset -- byte offset in the work area of an int that
+ * the one-pass kernel leaves at 0; it is non-zero only if a wait of that
+ * kernel gave up (its spin limit) or the workgroups were not spread over the
+ * XCDs as the launch assumes, in which case dQ is not valid. For tests and
+ * diagnostics; reading it requires the call's work to have completed.
+ */
+int attn_bwd_work_error_offset(void);
+
+/*
  * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc. Same arguments, results and errors as attn_bwd, without

@@ -47,7 +47,8 @@ EXPORTS = ("attn_fwd", "attn_fwd_validate", "attn_fwd_path",
            "attn_fwd_select_path", "attn_status_string", "attn_bwd",
            "attn_bwd_validate", "axial_pass", "axial_pass_validate", "axial_block",
            "attn_fwd_dv", "attn_fwd_dv_validate", "axial_pass_split",
-           "attn_bwd_noalloc", "attn_fwd_fp8", "attn_fwd_fp8_validate")
+           "attn_bwd_noalloc", "attn_fwd_fp8", "attn_fwd_fp8_validate",
+           "attn_bwd_ws", "attn_bwd_work_bytes", "attn_bwd_work_error_offset")
 
 _lib = None
 
@@ -77,6 +78,13 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = cint
         L.attn_bwd_noalloc.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, cint, cint, vp]
         L.attn_bwd_noalloc.restype = cint
+        L.attn_bwd_ws.argtypes = ([vp] * 10 + [i64] * 5 + [ctypes.c_float, cint, cint, vp, i64,
+                                                           vp])
+        L.attn_bwd_ws.restype = cint
+        L.attn_bwd_work_bytes.argtypes = [i64] * 5 + [cint, cint]
+        L.attn_bwd_work_bytes.restype = i64
+        L.attn_bwd_work_error_offset.argtypes = []
+        L.attn_bwd_work_error_offset.restype = cint
         L.attn_fwd_fp8.argtypes = [vp] * 5 + [i64] * 5 + [ctypes.c_float, cint, vp]
         L.attn_fwd_fp8.restype = cint
         L.attn_fwd_fp8_validate.argtypes = [vp] * 5 + [i64] * 5 + [ctypes.c_float, cint]
@@ -255,9 +263,18 @@ def attn_fwd_fp8(q, k, vt, is_causal: bool = False, scale: Optional[float] = Non
     return o, lse
 
 
+def attn_bwd_work_bytes(B, H, M, N, D, is_causal, dtype) -> int:
+    """Work-area bytes for the one-pass backward (0 where it does not apply)."""
+    return lib().attn_bwd_work_bytes(B, H, M, N, D, int(bool(is_causal)), int(dtype))
+
+
+def attn_bwd_work_error_offset() -> int:
+    return lib().attn_bwd_work_error_offset()
+
+
 def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
              scale: Optional[float] = None, out: Optional[Tuple] = None,
-             delta=None):
+             delta=None, one_pass: bool = True, work=None):
     """(dQ, dK, dV) of attention for the upstream gradient ``dout``.
 
     ``q, k, v`` are the forward's inputs, ``o, lse`` its outputs (from
@@ -266,6 +283,12 @@ def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
     writes into preallocated tensors; ``delta`` is an optional fp32 [B, H, M]
     workspace (allocated here if None) that receives rowsum(O * dO). bf16
     or fp16, D in {32, 64, 128}. Asynchronous on torch's current stream.
+
+    Where the one-pass backward applies (D = 128, no mask, B*H a multiple of
+    8) and ``one_pass`` is true, the call goes through the C ``attn_bwd_ws``
+    with a work area (``work``: a uint8 GPU tensor of at least
+    ``attn_bwd_work_bytes`` bytes, allocated here if None); otherwise through
+    ``attn_bwd``. Both are deterministic.
     """
     import torch
     B, H, M, N, D = _check(q, k, v)
@@ -294,14 +317,30 @@ def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
     elif (tuple(delta.shape) != (B, H, M) or delta.dtype != torch.float32
           or not delta.is_contiguous() or delta.device != q.device):
         raise ValueError("delta must be a contiguous fp32 [B, H, M] tensor on q's device")
+    need = attn_bwd_work_bytes(B, H, M, N, D, is_causal, dt) if one_pass else 0
+    if need > 0:
+        if work is None:
+            work = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif (work.dtype != torch.uint8 or work.device != q.device or not work.is_contiguous()
+              or work.numel() < need):
+            raise ValueError(f"work must be a contiguous uint8 tensor of >= {need} bytes "
+                             "on q's device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), delta.data_ptr(), B, H, M, N, D, float(scale),
-                            int(bool(is_causal)), dt, stream)
+        if need > 0:
+            st = lib().attn_bwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                   dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, M, N,
+                                   D, float(scale), int(bool(is_causal)), dt, work.data_ptr(),
+                                   work.numel(), stream)
+        else:
+            st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), delta.data_ptr(), B, H, M, N, D, float(scale),
+                                int(bool(is_causal)), dt, stream)
     if st != MI355_ATTN_OK:
-        raise RuntimeError(f"attn_bwd failed: {attn_status_string(st)} ({st})")
+        name = "attn_bwd_ws" if need > 0 else "attn_bwd"
+        raise RuntimeError(f"{name} failed: {attn_status_string(st)} ({st})")
     return dq, dk, dv
 
 

@@ -359,6 +359,59 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
 }
 
+int64_t attn_bwd_work_bytes(int64_t B, int64_t H, int64_t M, int64_t N, int64_t D,
+                            int is_causal, int dtype) {
+  if (B < 0 || H < 0 || M < 0 || N < 0) return 0;
+  if (dtype != MI355_ATTN_BF16 && dtype != MI355_ATTN_FP16) return 0;
+  int64_t BH, rows, elems;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, M, &rows) || !mul_ok(rows, D, &elems)) return 0;
+  return mi355::bwd_fused_work_bytes(BH, M, N, D, is_causal != 0);
+}
+
+int attn_bwd_ws(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B,
+                int64_t H, int64_t M, int64_t N, int64_t D, float scale, int is_causal,
+                int dtype, void* work, int64_t work_bytes, void* stream) {
+  const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D,
+                              scale, is_causal, dtype);
+  if (st != MI355_ATTN_OK) return st;
+  if (work_bytes < 0) return MI355_ATTN_ERR_INVALID_ARG;
+  const int64_t need = attn_bwd_work_bytes(B, H, M, N, D, is_causal, dtype);
+  if (need == 0 || work == nullptr || work_bytes < need)
+    return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, M, N, D, scale, is_causal,
+                    dtype, stream);
+  if ((uintptr_t)work & 255u) return MI355_ATTN_ERR_MISALIGNED;
+  // the work area is written: it must not overlap any argument buffer
+  const int64_t q_bytes = B * H * M * D * 2, kv_bytes = B * H * N * D * 2, rows = B * H * M * 4;
+  const void* p[10] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
+  const int64_t n[10] = {q_bytes, kv_bytes, kv_bytes, q_bytes, rows, q_bytes,
+                         q_bytes, kv_bytes, kv_bytes, rows};
+  for (int i = 0; i < 10; ++i)
+    if (overlap(work, need, p[i], n[i])) return MI355_ATTN_ERR_INVALID_ARG;
+  mi355::BwdLaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.BH = B * H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.causal = is_causal != 0;
+  a.stream = (hipStream_t)stream;
+  const hipError_t err = mi355::launch_bwd_fused(a, work, dtype == MI355_ATTN_FP16);
+  return err == hipSuccess ? MI355_ATTN_OK : MI355_ATTN_ERR_HIP;
+}
+
+int attn_bwd_work_error_offset(void) { return mi355::bwd_fused_error_offset(); }
+
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
                      int64_t B, int64_t H, int64_t M, int64_t N, int64_t D, float scale,

@@ -77,6 +77,15 @@ hipError_t launch_bwd_f16(const BwdLaunchArgs& a);
 // Rows per workgroup of the two backward kernels (grid sizing checks).
 int bwd_dq_tile_rows();
 int bwd_dkdv_tile_rows();
+// Single-pass backward (bf16 or fp16, D = 128, no mask, B*H a multiple of
+// 8): the bytes of device work area it needs (0 where it does not apply),
+// and its launch (delta kernel, then the fused kernel, on a.stream) with a
+// 256-byte aligned work area of at least that size. The int at byte offset
+// bwd_fused_error_offset() of the work area is 0 after a run in which every
+// wait ended normally.
+int64_t bwd_fused_work_bytes(int64_t BH, int64_t M, int64_t N, int64_t D, bool causal);
+hipError_t launch_bwd_fused(const BwdLaunchArgs& a, void* work, bool f16);
+int bwd_fused_error_offset();
 
 // Capacity (query rows, B*H*M) of the static delta array of the no-alloc
 // backward, and the device address of that array on the current device

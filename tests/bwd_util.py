@@ -32,12 +32,14 @@ U_F32 = 2.0 ** -24
 LAMBDA = 8.0
 
 
-def gpu_fwd_bwd(q, k, v, g, causal, scale):
-    """attn_fwd then attn_bwd on cuda:0; returns numpy fp64 (dq, dk, dv, delta)."""
+def gpu_fwd_bwd(q, k, v, g, causal, scale, one_pass=True):
+    """attn_fwd then attn_bwd on cuda:0; returns numpy fp64 (dq, dk, dv) and
+    the GPU (o, lse)."""
     dev = torch.device("cuda:0")
     qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
     o, lse = attn.attn_fwd(qd, kd, vd, is_causal=causal, scale=scale)
-    dq, dk, dv = attn.attn_bwd(qd, kd, vd, o, lse, gd, is_causal=causal, scale=scale)
+    dq, dk, dv = attn.attn_bwd(qd, kd, vd, o, lse, gd, is_causal=causal, scale=scale,
+                               one_pass=one_pass)
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().double().numpy()
     return f(dq), f(dk), f(dv), o, lse
@@ -77,14 +79,14 @@ def head_bounds(q, k, v, g, scale, causal, refs, u=U_BF16):
     return b_dq, b_dk, b_dv
 
 
-def check_heads(q, k, v, g, causal, scale, heads=None, label=""):
+def check_heads(q, k, v, g, causal, scale, heads=None, label="", one_pass=True):
     """GPU forward + backward on the full tensors; every element of the
     listed heads (default: all) against the oracle within head_bounds."""
     B, H, M, D = q.shape
     N = k.shape[2]
-    print(f"[bwd-parity] {label} {tuple(q.shape)} N={N} causal={causal} scale={scale}",
-          flush=True)
-    dq, dk, dv, _, _ = gpu_fwd_bwd(q, k, v, g, causal, scale)
+    print(f"[bwd-parity] {label} {tuple(q.shape)} N={N} causal={causal} scale={scale} "
+          f"one_pass={one_pass}", flush=True)
+    dq, dk, dv, _, _ = gpu_fwd_bwd(q, k, v, g, causal, scale, one_pass)
     for t in (dq, dk, dv):
         assert np.isfinite(t).all(), "non-finite gradient"
     if heads is None:

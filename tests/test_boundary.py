@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
         ["attn_fwd", "attn_fwd_validate", "attn_fwd_path", "attn_fwd_select_path",
          "attn_status_string", "attn_bwd", "attn_bwd_validate", "axial_pass",
          "axial_pass_validate", "axial_block", "attn_fwd_dv", "attn_fwd_dv_validate",
-         "axial_pass_split", "attn_bwd_noalloc", "attn_fwd_fp8", "attn_fwd_fp8_validate"])
+         "axial_pass_split", "attn_bwd_noalloc", "attn_fwd_fp8", "attn_fwd_fp8_validate",
+         "attn_bwd_ws", "attn_bwd_work_bytes", "attn_bwd_work_error_offset"])
 
 
 def test_library_exports_every_declared_symbol(hip_lib):
@@ -321,3 +322,47 @@ def test_fp8_validation_before_any_hip_call(hip_lib):
     assert v(o=o + 8) == MISALIGNED and v(vt=vt + 4) == MISALIGNED and v(lse=lse + 2) == MISALIGNED
     assert v(o=q) == INVALID                          # output over an input
     assert v(lse=o + 1024) == INVALID                 # lse inside o
+
+
+def test_bwd_work_bytes(hip_lib):
+    """The one-pass backward's work area: header (256 B), one int counter per
+    (head, 32-query tile, 32-wide d block), one fp32 L log2(e) per row (each
+    rounded up to 256 B), fp32 dQ sums; 0 wherever the path does not apply."""
+    wb = hip_lib.attn_bwd_work_bytes
+    up = lambda x: -(-x // 256) * 256
+    for B, H, M, N in [(4, 16, 4096, 4096), (1, 8, 1, 1), (2, 4, 33, 257), (1, 8, 300, 600)]:
+        counters = up(B * H * (-(-M // 32)) * 16)
+        assert wb(B, H, M, N, 128, False, BF16) == (256 + counters + up(B * H * M * 4)
+                                                     + B * H * M * 128 * 4)
+        assert wb(B, H, M, N, 128, False, FP16) == wb(B, H, M, N, 128, False, BF16)
+    assert wb(4, 16, 4096, 4096, 128, True, BF16) == 0      # causal
+    assert wb(4, 16, 4096, 4096, 64, False, BF16) == 0      # D != 128
+    assert wb(1, 6, 100, 100, 128, False, BF16) == 0        # B*H % 8 != 0
+    assert wb(1, 8, 100, 100, 128, False, FP32) == 0
+    assert wb(1, 8, 0, 100, 128, False, BF16) == 0          # nothing to do
+    assert wb(1, 8, 100, 0, 128, False, BF16) == 0
+    assert wb(-1, 8, 100, 100, 128, False, BF16) == 0
+    assert hip_lib.attn_bwd_work_error_offset() == 32
+
+
+def test_bwd_ws_checks_the_work_area_before_any_hip_call(hip_lib):
+    """attn_bwd_ws validates like attn_bwd, then refuses a misaligned or
+    overlapping work area (fake addresses: nothing is dereferenced)."""
+    lib = hip_lib.lib()
+    B, H, M, N, D = 1, 8, 64, 64, 128
+    qb, kb = B * H * M * D * 2, B * H * N * D * 2
+    base = 1 << 40
+    p = [base + i * (1 << 28) for i in range(10)]  # q k v o lse dout dq dk dv delta
+    need = hip_lib.attn_bwd_work_bytes(B, H, M, N, D, False, BF16)
+    work = base + 12 * (1 << 28)
+
+    def call(w, nbytes, causal=0, scale=0.125):
+        return lib.attn_bwd_ws(*p, B, H, M, N, D, scale, causal, BF16, w, nbytes, None)
+
+    assert call(work + 16, need) == MISALIGNED
+    assert call(p[6] + 256, need) == INVALID      # overlaps dq
+    assert call(p[0], need) == INVALID            # overlaps q
+    assert call(work, -1) == INVALID
+    assert call(work, need, scale=float("nan")) == INVALID   # attn_bwd's own checks first
+    assert lib.attn_bwd_ws(*p[:9], None, B, H, M, N, D, 0.125, 0, BF16, work, need,
+                           None) == INVALID

@@ -1,6 +1,7 @@
 """attn_bwd_noalloc (delta in the library's static device array, no
-allocation) against attn_bwd (delta in a caller workspace): the same kernels,
-so the gradients must be bit-identical. Two calls in a row, the second on a
+allocation) against attn_bwd (delta in a caller workspace; its two-kernel
+form, which the no-alloc entry is a variant of): the same kernels, so the
+gradients must be bit-identical. Two calls in a row, the second on a
 smaller problem (the array keeps the first call's delta; the second must not
 depend on it), then a problem above the array's capacity, which is refused
 before launching."""
@@ -23,7 +24,7 @@ def _problem(B, H, M, N, D, dtype, causal, seed):
 
 
 def _both(q, k, v, g, o, lse, causal):
-    ref = attn.attn_bwd(q, k, v, o, lse, g, is_causal=causal)
+    ref = attn.attn_bwd(q, k, v, o, lse, g, is_causal=causal, one_pass=False)
     out = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
     got = attn.attn_bwd_noalloc(q, k, v, o, lse, g, out, is_causal=causal)
     torch.cuda.synchronize()
