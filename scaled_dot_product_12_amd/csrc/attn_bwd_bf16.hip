@@ -680,11 +680,11 @@ __global__ __launch_bounds__(bwd_waves(D) * 64, bwd_blocks_per_cu(D)) void attn_
 // share's wave writes dQ in the input type. The sum, and so dQ, is the same
 // on every run.
 //  * A workgroup takes its (head, key tile) from a ticket counter when it
-//    starts, so the key workgroups of a head start together, and a head has
-//    at most 32 of them, one per CU of an XCD: every wait is for a workgroup
-//    that is running (or, without the rotation below, for an earlier
-//    ticket), and every wait is bounded, setting an error word if it gives
-//    up (it never does when the placement holds).
+//    starts, so the key workgroups of a head start together; with the
+//    rotation below a head has at most one per CU of an XCD: every wait is
+//    for a workgroup that is running (or, without the rotation, for an
+//    earlier ticket), and every wait is bounded, setting an error word if it
+//    gives up (it never does when the placement holds).
 //  * The tickets are counted per XCD and heads are dealt to XCDs, so the
 //    workgroups of a head share one L2, where the shares meet: counters and
 //    shares are read with device-scope loads that skip the CU's own cache,
@@ -790,7 +790,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
     const float* __restrict__ delta, const uint16_t* __restrict__ dout,
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     unsigned char* __restrict__ work, long long l2_off, long long acc_off, int M, int N,
-    int tiles_n, int heads, float c, float scale) {
+    int tiles_n, int heads, int n_xcc, int cus_per_xcc, float c, float scale) {
   constexpr int D = 128, NT = 512, BNK = kFusedBN, BQ = kFusedBQ;
   using T = Tile<D, BQ>;  // Q and dO ring tiles (rows permuted, as in the dK/dV kernel)
   using H = Half16<F16>;
@@ -819,15 +819,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
   float* const accw = (float*)(work + acc_off);
 
   // (head, key tile) in start order from this XCD's ticket counter: heads
-  // xcc, xcc + 8, ... run on XCD xcc, key tiles in ticket order.
+  // xcc, xcc + n_xcc, ... run on XCD xcc, key tiles in ticket order.
   if (tid == 0) {
-    const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // HW_REG_XCC_ID
+    const int xcc = (__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) % n_xcc;  // HW_REG_XCC_ID
     ticket_s = (atomicAdd(hdr + xcc, 1) << 3) | xcc;
   }
   __syncthreads();
   const int tk = __builtin_amdgcn_readfirstlane(ticket_s);
   const int ticket = tk >> 3;
-  const int bh = (tk & 7) + 8 * (ticket / tiles_n);
+  const int bh = (tk & 7) + n_xcc * (ticket / tiles_n);
   const int jk = ticket % tiles_n;  // key tile, and this workgroup's place in every dQ sum
   if (bh >= heads) {
     // more workgroups on this XCD than it has work for: the placement the
@@ -924,12 +924,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
   // is key order rotated to start at the first arriver. (rot = 0: all start
   // at tile 0 and the order is key order.) With rot > 0 a share may wait for
   // a workgroup with a later ticket, so all key workgroups of a head must be
-  // resident together: at most 32, one per CU of an XCD. A wait in the
+  // resident together: at most one per CU of an XCD. A wait in the
   // middle of step n is for a counter passed in the middle of step
   // n + 1 - rot of another workgroup: rot = 2 keeps every wait behind an
   // earlier event (rot = 1 would allow a cycle of waits), and rot = 0 only
   // waits for lower key tiles.
-  const int rot = tiles_n <= 32 && t_end >= 2 * tiles_n ? 2 : 0;
+  const int rot = tiles_n <= cus_per_xcc && t_end >= 2 * tiles_n ? 2 : 0;
   auto tile_at = [&](int n) {  // query tile of step n
     const int t = n - jk * rot;
     return t < 0 ? t + t_end : t;
@@ -1296,8 +1296,32 @@ int64_t bwd_fused_work_bytes(int64_t BH, int64_t M, int64_t N, int64_t D, bool c
   return kFusedHeader + fused_counter_bytes(BH, M) + fused_l2_bytes(BH, M) + BH * M * D * 4;
 }
 
+// XCDs of the current device and compute units per XCD (looked up once per
+// device). The fused kernel deals heads to XCDs and needs B*H to be a
+// multiple of the XCD count.
+static bool fused_placement(int64_t BH, int* n_xcc, int* cus_per_xcc) {
+  static int cache[64][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (cache[dev][0] == 0) {
+    int x = 0, cu = 0;
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return false;
+    cache[dev][1] = x > 0 ? cu / x : 0;
+    cache[dev][0] = x;
+  }
+  *n_xcc = cache[dev][0];
+  *cus_per_xcc = cache[dev][1];
+  return (*n_xcc == 1 || *n_xcc == 2 || *n_xcc == 4 || *n_xcc == 8) && BH % *n_xcc == 0 &&
+         *cus_per_xcc > 0;
+}
+
 template <bool F16>
 static hipError_t launch_bwd_fused_16(const BwdLaunchArgs& a, void* work) {
+  int n_xcc = 0, cus_per_xcc = 0;
+  if (!fused_placement(a.BH, &n_xcc, &cus_per_xcc))
+    return F16 ? launch_bwd_16<true>(a) : launch_bwd_16<false>(a);  // the two-kernel backward
   const int64_t rows = a.BH * a.M;
   const int64_t counters = fused_counter_bytes(a.BH, a.M);
   const int nclear = (int)((kFusedHeader + counters) / 4);
@@ -1314,7 +1338,7 @@ static hipError_t launch_bwd_fused_16(const BwdLaunchArgs& a, void* work) {
                      (const uint16_t*)a.v, a.lse, a.delta, (const uint16_t*)a.dout,
                      (uint16_t*)a.dq, (uint16_t*)a.dk, (uint16_t*)a.dv, (unsigned char*)work,
                      (long long)l2_off, (long long)acc_off, (int)a.M, (int)a.N, tiles_n,
-                     (int)a.BH, a.scale * kLog2e, a.scale);
+                     (int)a.BH, n_xcc, cus_per_xcc, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
