@@ -48,6 +48,13 @@ def _work_error(work):
     return int(work[off:off + 4].cpu().view(torch.int32)[0])
 
 
+def _tickets(work):
+    """Workgroups that took a ticket in the last one-pass run (the eight
+    per-XCD counters at the start of the work area): B*H*ceil(N/256) when the
+    one-pass kernel ran."""
+    return int(work[:32].cpu().view(torch.int32).sum())
+
+
 # (B, H, M, N): B*H a multiple of 8; one and several key workgroups (256
 # keys each), ragged query tiles (32 rows) and key tails
 SHAPES = [
@@ -71,9 +78,10 @@ def test_one_pass_against_oracle_and_two_pass(hip_lib, shape, dtype):
     need = attn.attn_bwd_work_bytes(B, H, M, N, 128, False, code)
     assert need > 0
     print(f"[one-pass] {dtype} {shape} work {need} B", flush=True)
-    work = torch.empty(need, dtype=torch.uint8, device=DEV)
+    work = torch.zeros(need, dtype=torch.uint8, device=DEV)
     a = _run(q, k, v, g, code, True, work)
     assert _work_error(work) == 0
+    assert _tickets(work) == B * H * -(-N // 256), "the one-pass kernel did not run"
     b = _run(q, k, v, g, code, False)
     _close(a, b)
     heads = [(0, 0), (B - 1, H - 1)]
@@ -118,10 +126,11 @@ def test_one_pass_c4_shape(hip_lib):
     q, k, v = make_qkv(4, 16, 4096, 4096, 128, "bf16", 4)
     g = make_dout(4, 16, 4096, 128, "bf16", 4)
     code = attn.MI355_ATTN_BF16
-    work = torch.empty(attn.attn_bwd_work_bytes(4, 16, 4096, 4096, 128, False, code),
+    work = torch.zeros(attn.attn_bwd_work_bytes(4, 16, 4096, 4096, 128, False, code),
                        dtype=torch.uint8, device=DEV)
     a = _run(q, k, v, g, code, True, work)
     assert _work_error(work) == 0
+    assert _tickets(work) == 4 * 16 * 16, "the one-pass kernel did not run"
     b = _run(q, k, v, g, code, False)
     _close(a, b)
     del a, b
