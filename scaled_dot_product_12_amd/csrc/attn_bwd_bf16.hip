@@ -828,7 +828,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
   const int tk = __builtin_amdgcn_readfirstlane(ticket_s);
   const int ticket = tk >> 3;
   const int bh = (tk & 7) + n_xcc * (ticket / tiles_n);
-  const int jk = ticket % tiles_n;  // key tile, and this workgroup's place in every dQ sum
+  const int jk = ticket % tiles_n;  // key tile
   if (bh >= heads) {
     // more workgroups on this XCD than it has work for: the placement the
     // launch relies on does not hold; flag it and do nothing
@@ -887,7 +887,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
       lds_dma4(bytes_desc(wave == 0 ? lh : dh, (uint32_t)M * 4),
                smem + STAT_OFF + (buf * 128 + wave * 64) * 4, (j * BQ + lane_id_here()) * 4);
   };
-
 
   // dS^T as the B operand of the dQ product, from a dS buffer (key rows of
   // 32 queries, 16-byte chunk position p ^ ((row >> 2) & 3)): the same key
