@@ -203,12 +203,15 @@ int attn_bwd_validate(const void *q, const void *k, const void *v,
  *   work, work_bytes  caller-owned device memory, 256-byte aligned, not
  *              overlapping any other argument; its prior contents are
  *              ignored and the call overwrites the first
- *              attn_bwd_work_bytes(...) bytes.
+ *              attn_bwd_work_bytes(...) bytes. Calls whose work may overlap
+ *              in time (different streams) need different work areas.
  *   all other arguments as for attn_bwd.
  *
  * The one-pass path applies to bf16 and fp16 with D = 128, no causal mask,
- * B*H a multiple of 8 and B*H*M <= 2^30; otherwise, or with work == NULL or
- * work_bytes below attn_bwd_work_bytes(...), the call is exactly attn_bwd.
+ * B*H a multiple of 8 and B*H*M <= 2^30, on a device whose XCD count
+ * (hipDeviceAttributeNumberOfXccs) is 1, 2, 4 or 8; otherwise, or with
+ * work == NULL or work_bytes below attn_bwd_work_bytes(...), the call is
+ * exactly attn_bwd.
  * Enqueues two kernels on `stream` (delta, then the one-pass kernel). The
  * dQ, dK and dV it returns are deterministic but need not equal attn_bwd's
  * bit for bit (dQ is summed in another order).
