@@ -284,8 +284,8 @@ def attn_bwd(q, k, v, o, lse, dout, is_causal: bool = False,
     workspace (allocated here if None) that receives rowsum(O * dO). bf16
     or fp16, D in {32, 64, 128}. Asynchronous on torch's current stream.
 
-    Where the one-pass backward applies (D = 128, no mask, B*H a multiple of
-    8) and ``one_pass`` is true, the call goes through the C ``attn_bwd_ws``
+    Where the one-pass backward applies (D = 128, no mask) and ``one_pass``
+    is true, the call goes through the C ``attn_bwd_ws``
     with a work area (``work``: a uint8 GPU tensor of at least
     ``attn_bwd_work_bytes`` bytes, allocated here if None); otherwise through
     ``attn_bwd``. Both are deterministic.

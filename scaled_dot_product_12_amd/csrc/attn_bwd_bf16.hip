@@ -790,7 +790,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
     const float* __restrict__ delta, const uint16_t* __restrict__ dout,
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     unsigned char* __restrict__ work, long long l2_off, long long acc_off, int M, int N,
-    int tiles_n, int heads, int n_xcc, int cus_per_xcc, float c, float scale) {
+    int tiles_n, int heads, int heads_padded, int n_xcc, int cus_per_xcc, float c, float scale) {
   constexpr int D = 128, NT = 512, BNK = kFusedBN, BQ = kFusedBQ;
   using T = Tile<D, BQ>;  // Q and dO ring tiles (rows permuted, as in the dK/dV kernel)
   using H = Half16<F16>;
@@ -830,9 +830,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
   const int bh = (tk & 7) + n_xcc * (ticket / tiles_n);
   const int jk = ticket % tiles_n;  // key tile
   if (bh >= heads) {
-    // more workgroups on this XCD than it has work for: the placement the
-    // launch relies on does not hold; flag it and do nothing
-    if (tid == 0) atomicOr(hdr + 8, 2);
+    // heads past B*H pad the grid to a multiple of the XCD count; beyond
+    // those, this XCD got more workgroups than it has work for: the placement
+    // the launch relies on does not hold, so flag it
+    if (tid == 0 && bh >= heads_padded) atomicOr(hdr + 8, 2);
     return;
   }
 
@@ -1288,17 +1289,17 @@ static int64_t fused_counter_bytes(int64_t BH, int64_t M) {
 static int64_t fused_l2_bytes(int64_t BH, int64_t M) { return (BH * M * 4 + 255) / 256 * 256; }
 
 int64_t bwd_fused_work_bytes(int64_t BH, int64_t M, int64_t N, int64_t D, bool causal) {
-  // D = 128 without the mask; whole heads per XCD (B*H a multiple of 8);
-  // row counts that the kernels index with 32-bit integers.
-  if (D != 128 || causal || BH < 8 || BH % 8 != 0 || M < 1 || N < 1) return 0;
+  // D = 128 without the mask; row counts that the kernels index with 32-bit
+  // integers.
+  if (D != 128 || causal || BH < 1 || M < 1 || N < 1) return 0;
   if (BH * M > (int64_t{1} << 30) || M > (int64_t{1} << 24) || N > (int64_t{1} << 24)) return 0;
   return kFusedHeader + fused_counter_bytes(BH, M) + fused_l2_bytes(BH, M) + BH * M * D * 4;
 }
 
 // XCDs of the current device and compute units per XCD (looked up once per
-// device). The fused kernel deals heads to XCDs and needs B*H to be a
-// multiple of the XCD count.
-static bool fused_placement(int64_t BH, int* n_xcc, int* cus_per_xcc) {
+// device). The fused kernel deals heads to XCDs (B*H padded to a multiple of
+// the XCD count).
+static bool fused_placement(int* n_xcc, int* cus_per_xcc) {
   static int cache[64][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
@@ -1312,14 +1313,13 @@ static bool fused_placement(int64_t BH, int* n_xcc, int* cus_per_xcc) {
   }
   *n_xcc = cache[dev][0];
   *cus_per_xcc = cache[dev][1];
-  return (*n_xcc == 1 || *n_xcc == 2 || *n_xcc == 4 || *n_xcc == 8) && BH % *n_xcc == 0 &&
-         *cus_per_xcc > 0;
+  return (*n_xcc == 1 || *n_xcc == 2 || *n_xcc == 4 || *n_xcc == 8) && *cus_per_xcc > 0;
 }
 
 template <bool F16>
 static hipError_t launch_bwd_fused_16(const BwdLaunchArgs& a, void* work) {
   int n_xcc = 0, cus_per_xcc = 0;
-  if (!fused_placement(a.BH, &n_xcc, &cus_per_xcc))
+  if (!fused_placement(&n_xcc, &cus_per_xcc))
     return F16 ? launch_bwd_16<true>(a) : launch_bwd_16<false>(a);  // the two-kernel backward
   const int64_t rows = a.BH * a.M;
   const int64_t counters = fused_counter_bytes(a.BH, a.M);
@@ -1332,12 +1332,14 @@ static hipError_t launch_bwd_fused_16(const BwdLaunchArgs& a, void* work) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int tiles_n = (int)((a.N + kFusedBN - 1) / kFusedBN);
-  hipLaunchKernelGGL((attn_bwd_fused_kernel<F16>), dim3((unsigned)(a.BH * tiles_n)), dim3(512),
+  const int64_t heads_padded = (a.BH + n_xcc - 1) / n_xcc * n_xcc;
+  hipLaunchKernelGGL((attn_bwd_fused_kernel<F16>), dim3((unsigned)(heads_padded * tiles_n)),
+                     dim3(512),
                      0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.lse, a.delta, (const uint16_t*)a.dout,
                      (uint16_t*)a.dq, (uint16_t*)a.dk, (uint16_t*)a.dv, (unsigned char*)work,
                      (long long)l2_off, (long long)acc_off, (int)a.M, (int)a.N, tiles_n,
-                     (int)a.BH, n_xcc, cus_per_xcc, a.scale * kLog2e, a.scale);
+                     (int)a.BH, (int)heads_padded, n_xcc, cus_per_xcc, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 

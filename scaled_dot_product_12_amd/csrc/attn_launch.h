@@ -77,8 +77,8 @@ hipError_t launch_bwd_f16(const BwdLaunchArgs& a);
 // Rows per workgroup of the two backward kernels (grid sizing checks).
 int bwd_dq_tile_rows();
 int bwd_dkdv_tile_rows();
-// Single-pass backward (bf16 or fp16, D = 128, no mask, B*H a multiple of
-// 8): the bytes of device work area it needs (0 where it does not apply),
+// Single-pass backward (bf16 or fp16, D = 128, no mask): the bytes of device
+// work area it needs (0 where it does not apply),
 // and its launch (delta kernel, then the fused kernel, on a.stream) with a
 // 256-byte aligned work area of at least that size. The int at byte offset
 // bwd_fused_error_offset() of the work area is 0 after a run in which every

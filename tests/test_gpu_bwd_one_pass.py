@@ -50,13 +50,20 @@ def _work_error(work):
 
 def _tickets(work):
     """Workgroups that took a ticket in the last one-pass run (the eight
-    per-XCD counters at the start of the work area): B*H*ceil(N/256) when the
-    one-pass kernel ran."""
+    per-XCD counters at the start of the work area)."""
     return int(work[:32].cpu().view(torch.int32).sum())
 
 
-# (B, H, M, N): B*H a multiple of 8; one and several key workgroups (256
-# keys each), ragged query tiles (32 rows) and key tails
+def _ran(work, BH, N):
+    """The one-pass kernel ran: every head's key workgroups took a ticket,
+    plus those of the heads that pad B*H to a multiple of the XCD count."""
+    t = -(-N // 256)
+    n = _tickets(work)
+    return n % t == 0 and BH * t <= n < (BH + 8) * t
+
+
+# (B, H, M, N): one and several key workgroups (256 keys each), ragged query
+# tiles (32 rows) and key tails, B*H a multiple of the XCD count or not
 SHAPES = [
     (1, 8, 300, 600),
     (2, 4, 33, 257),
@@ -64,6 +71,8 @@ SHAPES = [
     (4, 2, 100, 1000),
     (1, 8, 1, 1),
     (1, 16, 31, 5),
+    (1, 3, 300, 700),
+    (3, 5, 97, 513),
 ]
 
 
@@ -81,7 +90,7 @@ def test_one_pass_against_oracle_and_two_pass(hip_lib, shape, dtype):
     work = torch.zeros(need, dtype=torch.uint8, device=DEV)
     a = _run(q, k, v, g, code, True, work)
     assert _work_error(work) == 0
-    assert _tickets(work) == B * H * -(-N // 256), "the one-pass kernel did not run"
+    assert _ran(work, B * H, N), "the one-pass kernel did not run"
     b = _run(q, k, v, g, code, False)
     _close(a, b)
     heads = [(0, 0), (B - 1, H - 1)]
@@ -105,14 +114,12 @@ def test_one_pass_deterministic(hip_lib):
 
 
 def test_one_pass_falls_back_where_it_does_not_apply(hip_lib):
-    """Causal, D = 64, B*H not a multiple of 8: no work area is needed and the
-    call is attn_bwd."""
+    """Causal or D = 64: no work area is needed and the call is attn_bwd."""
     code = attn.MI355_ATTN_BF16
     assert attn.attn_bwd_work_bytes(1, 8, 100, 100, 128, True, code) == 0
     assert attn.attn_bwd_work_bytes(1, 8, 100, 100, 64, False, code) == 0
-    assert attn.attn_bwd_work_bytes(1, 6, 100, 100, 128, False, code) == 0
-    q, k, v = make_qkv(1, 6, 100, 130, 128, "bf16", 62)
-    g = make_dout(1, 6, 100, 128, "bf16", 62)
+    q, k, v = make_qkv(1, 6, 100, 130, 64, "bf16", 62)
+    g = make_dout(1, 6, 100, 64, "bf16", 62)
     a = _run(q, k, v, g, code, True)
     b = _run(q, k, v, g, code, False)
     for x, y in zip(a, b):
@@ -130,7 +137,7 @@ def test_one_pass_c4_shape(hip_lib):
                        dtype=torch.uint8, device=DEV)
     a = _run(q, k, v, g, code, True, work)
     assert _work_error(work) == 0
-    assert _tickets(work) == 4 * 16 * 16, "the one-pass kernel did not run"
+    assert _ran(work, 4 * 16, 4096), "the one-pass kernel did not run"
     b = _run(q, k, v, g, code, False)
     _close(a, b)
     del a, b
