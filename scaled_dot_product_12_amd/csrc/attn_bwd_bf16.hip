@@ -1296,24 +1296,18 @@ int64_t bwd_fused_work_bytes(int64_t BH, int64_t M, int64_t N, int64_t D, bool c
   return kFusedHeader + fused_counter_bytes(BH, M) + fused_l2_bytes(BH, M) + BH * M * D * 4;
 }
 
-// XCDs of the current device and compute units per XCD (looked up once per
-// device). The fused kernel deals heads to XCDs (B*H padded to a multiple of
-// the XCD count).
+// XCDs of the current device and compute units per XCD (host queries, no
+// GPU work). The fused kernel deals heads to XCDs (B*H padded to a multiple
+// of the XCD count).
 static bool fused_placement(int* n_xcc, int* cus_per_xcc) {
-  static int cache[64][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  if (cache[dev][0] == 0) {
-    int x = 0, cu = 0;
-    if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return false;
-    cache[dev][1] = x > 0 ? cu / x : 0;
-    cache[dev][0] = x;
-  }
-  *n_xcc = cache[dev][0];
-  *cus_per_xcc = cache[dev][1];
-  return (*n_xcc == 1 || *n_xcc == 2 || *n_xcc == 4 || *n_xcc == 8) && *cus_per_xcc > 0;
+  int dev = 0, x = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  *n_xcc = x;
+  *cus_per_xcc = x > 0 ? cu / x : 0;
+  return (x == 1 || x == 2 || x == 4 || x == 8) && *cus_per_xcc > 0;
 }
 
 template <bool F16>
