@@ -56,3 +56,25 @@ def test_axial_block_graph_replays():
     col = tuple(t.to(DEV) for t in col)
     out = torch.empty_like(x)
     _replay_matches(lambda: attn.axial_block(x, row, col, out=out), [out])
+
+
+@pytest.mark.parametrize("one_pass", [True, False])
+def test_attn_bwd_graph_replays(one_pass):
+    """The backward in a graph: the one-pass path (delta kernel clearing the
+    counters of a preallocated work area, then the fused kernel) and the two
+    kernels; the work area keeps the previous replay's sums and counters, and
+    every replay must still give the eager gradients."""
+    from scaled_dot_product_12_amd.inputs import make_dout
+    B, H, M, N, D = 1, 8, 300, 600, 128
+    q, k, v = (t.to(DEV) for t in make_qkv(B, H, M, N, D, "bf16", seed=33))
+    g = make_dout(B, H, M, D, "bf16", seed=33).to(DEV)
+    o, lse = attn.attn_fwd(q, k, v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, M), dtype=torch.float32, device=DEV)
+    need = attn.attn_bwd_work_bytes(B, H, M, N, D, False, attn.MI355_ATTN_BF16)
+    assert need > 0
+    work = torch.empty(need, dtype=torch.uint8, device=DEV)
+    _replay_matches(lambda: attn.attn_bwd(q, k, v, o, lse, g, out=(dq, dk, dv), delta=delta,
+                                          one_pass=one_pass, work=work), [dq, dk, dv])
+    off = attn.attn_bwd_work_error_offset()
+    assert int(work[off:off + 4].cpu().view(torch.int32)[0]) == 0
