@@ -241,6 +241,10 @@ int64_t attn_bwd_work_bytes(int64_t B, int64_t H, int64_t M, int64_t N,
  * kernel gave up (its spin limit) or the workgroups were not spread over the
  * XCDs as the launch assumes, in which case dQ is not valid. For tests and
  * diagnostics; reading it requires the call's work to have completed.
+ * The waits assume that every key workgroup of a head gets a compute unit
+ * within a bounded time: kernels that run concurrently on the same device
+ * and hold its compute units for longer than the spin limit (about 10^6
+ * polls, a fraction of a second) can make a wait give up.
  */
 int attn_bwd_work_error_offset(void);
 
