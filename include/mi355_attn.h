@@ -207,8 +207,9 @@ int attn_bwd_validate(const void *q, const void *k, const void *v,
  *              in time (different streams) need different work areas.
  *   all other arguments as for attn_bwd.
  *
- * The one-pass path applies to bf16 and fp16 with D = 128, no causal mask
- * and B*H*M <= 2^30, on a device whose XCD count
+ * The one-pass path applies to bf16 and fp16 with D = 128, no causal mask,
+ * B*H*M <= 2^30, M and N <= 2^24 and B*H*ceil(M/32) <= 2^26, on a device
+ * whose XCD count
  * (hipDeviceAttributeNumberOfXccs) is 1, 2, 4 or 8; otherwise, or with
  * work == NULL or work_bytes below attn_bwd_work_bytes(...), the call is
  * exactly attn_bwd.

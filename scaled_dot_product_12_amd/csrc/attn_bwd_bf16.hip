@@ -761,7 +761,10 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(
   constexpr int QSTEPS = D / 16;
   const int tid = workitem_id();
   const int lane = tid & 63, wave = tid >> 6;
-  for (int i = workgroup_id() * 256 + tid; i < nclear; i += (int)gridDim.x * 256) clear[i] = 0;
+  // (unsigned: the stride, up to 2^31, does not fit an int; i < nclear <= 2^28
+  // never wraps)
+  const unsigned stride = gridDim.x * 256u;
+  for (unsigned i = workgroup_id() * 256u + tid; i < (unsigned)nclear; i += stride) clear[i] = 0;
   const int r = (workgroup_id() * 4 + wave) * 32 + (lane & 31);
   const int g = lane >> 5;
   bf16x8_t of[QSTEPS], gf[QSTEPS];
@@ -1293,6 +1296,8 @@ int64_t bwd_fused_work_bytes(int64_t BH, int64_t M, int64_t N, int64_t D, bool c
   // integers.
   if (D != 128 || causal || BH < 1 || M < 1 || N < 1) return 0;
   if (BH * M > (int64_t{1} << 30) || M > (int64_t{1} << 24) || N > (int64_t{1} << 24)) return 0;
+  // counters cleared by the delta kernel: at most 2^26 tiles (its word count fits an int)
+  if (BH * ((M + kFusedBQ - 1) / kFusedBQ) > (int64_t{1} << 26)) return 0;
   return kFusedHeader + fused_counter_bytes(BH, M) + fused_l2_bytes(BH, M) + BH * M * D * 4;
 }
 

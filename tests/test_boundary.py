@@ -342,6 +342,13 @@ def test_bwd_work_bytes(hip_lib):
     assert wb(1, 8, 0, 100, 128, False, BF16) == 0          # nothing to do
     assert wb(1, 8, 100, 0, 128, False, BF16) == 0
     assert wb(-1, 8, 100, 100, 128, False, BF16) == 0
+    # size limits: B*H*M <= 2^30, M and N <= 2^24, at most 2^26 query tiles
+    assert wb(1, 1 << 6, 1 << 24, 1, 128, False, BF16) > 0
+    assert wb(1, (1 << 6) + 1, 1 << 24, 1, 128, False, BF16) == 0
+    assert wb(1, 1, (1 << 24) + 1, 1, 128, False, BF16) == 0
+    assert wb(1, 1, 1, (1 << 24) + 1, 128, False, BF16) == 0
+    assert wb(1, 1 << 26, 1, 1, 128, False, BF16) > 0
+    assert wb(1, (1 << 26) + 1, 1, 1, 128, False, BF16) == 0
     assert hip_lib.attn_bwd_work_error_offset() == 32
 
 
