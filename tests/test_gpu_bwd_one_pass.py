@@ -142,3 +142,32 @@ def test_one_pass_c4_shape(hip_lib):
     _close(a, b)
     del a, b
     check_heads(q, k, v, g, False, _scale(128), heads=[(1, 3), (2, 12)], label="c4-one-pass")
+
+
+def test_one_pass_random_shapes(hip_lib):
+    """Seeded random shapes (B*H 1 to 21, so padded heads and not; M up to
+    700 and N up to 1300, so one to six key workgroups, with and without the
+    rotated tile walk), bf16 and fp16, a work area holding garbage: the
+    one-pass kernel runs, leaves its error word at zero, agrees with the
+    two-kernel path up to summation order, and one random head of each is
+    within the oracle bound."""
+    rng = np.random.default_rng(2027)
+    for case in range(20):
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 8))
+        M, N = int(rng.integers(1, 701)), int(rng.integers(1, 1301))
+        dtype = "fp16" if case % 3 == 2 else "bf16"
+        code = attn.MI355_ATTN_FP16 if dtype == "fp16" else attn.MI355_ATTN_BF16
+        seed = 7000 + case
+        q, k, v = make_qkv(B, H, M, N, 128, dtype, seed)
+        g = make_dout(B, H, M, 128, dtype, seed)
+        need = attn.attn_bwd_work_bytes(B, H, M, N, 128, False, code)
+        print(f"[one-pass-random] case {case} {dtype} {(B, H, M, N)} work {need} B", flush=True)
+        work = torch.full((need,), 0x55, dtype=torch.uint8, device=DEV)
+        a = _run(q, k, v, g, code, True, work)
+        assert _work_error(work) == 0
+        assert _ran(work, B * H, N), "the one-pass kernel did not run"
+        b = _run(q, k, v, g, code, False)
+        _close(a, b)
+        head = (int(rng.integers(0, B)), int(rng.integers(0, H)))
+        check_heads(q, k, v, g, False, _scale(128), heads=[head],
+                    label=f"one-pass-random-{case}")
