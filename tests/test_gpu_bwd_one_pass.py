@@ -171,3 +171,37 @@ def test_one_pass_random_shapes(hip_lib):
         head = (int(rng.integers(0, B)), int(rng.integers(0, H)))
         check_heads(q, k, v, g, False, _scale(128), heads=[head],
                     label=f"one-pass-random-{case}")
+
+
+def test_one_pass_concurrent_streams(hip_lib):
+    """Two one-pass calls in flight at once on two streams, each with its own
+    work area, while they share the compute units: no wait gives up, and
+    each result equals the same call run alone."""
+    code = attn.MI355_ATTN_BF16
+    runs = []
+    for seed, (B, H, M, N) in ((81, (2, 8, 1024, 1024)), (82, (1, 8, 777, 1500))):
+        q, k, v = make_qkv(B, H, M, N, 128, "bf16", seed)
+        g = make_dout(B, H, M, 128, "bf16", seed)
+        qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+        o, lse = attn.attn_fwd(qd, kd, vd)
+        need = attn.attn_bwd_work_bytes(B, H, M, N, 128, False, code)
+        runs.append((qd, kd, vd, o, lse, gd, torch.zeros(need, dtype=torch.uint8, device=DEV)))
+    torch.cuda.synchronize()
+    alone = []
+    for (qd, kd, vd, o, lse, gd, work) in runs:
+        alone.append(attn.attn_bwd(qd, kd, vd, o, lse, gd, work=work))
+        torch.cuda.synchronize()
+        assert _work_error(work) == 0
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    print("[one-pass-concurrent] two calls on two streams", flush=True)
+    for rep in range(3):
+        for i, ((qd, kd, vd, o, lse, gd, work), s) in enumerate(zip(runs, streams)):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                outs[i] = attn.attn_bwd(qd, kd, vd, o, lse, gd, work=work)
+        torch.cuda.synchronize()
+        for (run, a, b) in zip(runs, outs, alone):
+            assert _work_error(run[6]) == 0
+            for x, y in zip(a, b):
+                assert torch.equal(x, y)
