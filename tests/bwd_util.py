@@ -19,6 +19,14 @@ at most u * dabs_i). In dQ that error is common to the whole row, so it is
 added coherently: 2 u scale dabs_i sum_j P_ij |k_jd|. fp32 accumulation adds
 lambda * sqrt(n) * u32 * sum_i abar_i, and rounding the result to the input type
 u * |ref|.
+
+Gradual underflow: below the smallest normal number of the input type
+(2^-14 for fp16, 2^-126 for bf16) a rounded value errs by up to half the
+subnormal spacing, h = 2^-25 (fp16) or 2^-134 (bf16), not by u times its
+magnitude. So each rounded factor errs by at most u |x| + h: the terms add
+lambda * h * s * sqrt(sum_i x_i^2) over the terms that are not masked out
+(s the factor's multiplier: 1 for P in dV, scale for dS in dK and dQ; x the
+other operand), and the rounded result h when it is not an exact zero.
 """
 import numpy as np
 import torch
@@ -29,6 +37,9 @@ import scaled_dot_product_12_amd as attn
 U_BF16 = 2.0 ** -8
 U_F16 = 2.0 ** -11
 U_F32 = 2.0 ** -24
+# half the subnormal spacing of each 16-bit type
+H_BF16 = 2.0 ** -134
+H_F16 = 2.0 ** -25
 LAMBDA = 8.0
 
 
@@ -62,20 +73,23 @@ def head_bounds(q, k, v, g, scale, causal, refs, u=U_BF16):
     dabs = np.abs(O * g).sum(-1)
     dq_ref, dk_ref, dv_ref = refs
     sc = abs(scale)
+    h = H_F16 if u == U_F16 else H_BF16
 
-    def bound(w, x, n, ref, coherent=0.0):
+    def bound(w, x, n, ref, coherent=0.0, hs=1.0):
         # element (a, d) = sum_i w[i, a] * x[i, d] with w, x >= 0
         rss = np.sqrt((w * w).T @ (x * x))
         s1 = w.T @ x
+        live = (w > 0).astype(np.float64)
+        under = LAMBDA * h * hs * np.sqrt(live.T @ (x * x))
         return (LAMBDA * u * rss + LAMBDA * np.sqrt(n) * U_F32 * s1
-                + u * np.abs(ref) + coherent)
+                + u * np.abs(ref) + h * (ref != 0) + under + coherent)
 
     b_dv = bound(P, np.abs(g), M, dv_ref)
     wk = sc * P * (np.abs(dP) + np.abs(delta)[:, None] + dabs[:, None])
-    b_dk = bound(wk, np.abs(q), M, dk_ref)
+    b_dk = bound(wk, np.abs(q), M, dk_ref, hs=sc)
     wq = sc * P * (np.abs(dP) + np.abs(delta)[:, None])
     coh = 2.0 * u * sc * dabs[:, None] * (P @ np.abs(k))
-    b_dq = bound(wq.T, np.abs(k), N, dq_ref, coherent=coh)
+    b_dq = bound(wq.T, np.abs(k), N, dq_ref, coherent=coh, hs=sc)
     return b_dq, b_dk, b_dv
 
 

@@ -43,6 +43,16 @@ def test_bwd_parity_fp16(hip_lib, D, causal, M, N):
     check_heads(q, k, v, g, causal, _scale(D), label=f"fp16-D{D}")
 
 
+def test_bwd_fp16_gradients_in_the_subnormal_range(hip_lib):
+    """fp16, causal, N > M: key M - 1 is seen by the last query only, and in
+    these inputs its dV and dK rows fall far below fp16's smallest normal
+    number (2^-14), where a rounded value errs by up to half the subnormal
+    spacing (2^-25) rather than by u times its magnitude; the bound carries
+    that term. Every element of both heads within the bound."""
+    q, k, v, g = _inputs(2, 1, 194, 475, 32, seed=130019, dtype="fp16")
+    check_heads(q, k, v, g, True, _scale(32), label="fp16-subnormal")
+
+
 @pytest.mark.parametrize("M,N", [(1, 1), (1, 200), (200, 1), (5, 3), (64, 64), (65, 129)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small_and_ragged(hip_lib, M, N, causal):
