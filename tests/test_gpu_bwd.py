@@ -142,3 +142,22 @@ def test_bwd_p64_shape_sampled_head(hip_lib):
     shape with head dim 64); one whole head against the oracle."""
     q, k, v, g = _inputs(4, 32, 8192, 8192, 64, seed=6)
     check_heads(q, k, v, g, False, _scale(64), heads=[(2, 17)], label="p64")
+
+
+def test_bwd_random_problem_sweep(hip_lib):
+    """60 seeded random problems (bf16 and fp16; D 32, 64 or 128; with and
+    without the causal mask; M up to 600 and N up to 900, so ragged tails and
+    N > M), each through the default path and the two-kernel path, one random
+    head of each within the bound."""
+    rng = np.random.default_rng(31337)
+    for case in range(60):
+        dtype = ["bf16", "fp16"][case % 2]
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 6))
+        M, N = int(rng.integers(1, 600)), int(rng.integers(1, 900))
+        D = int(rng.choice([32, 64, 128, 128]))
+        causal = bool(rng.integers(0, 2))
+        q, k, v, g = _inputs(B, H, M, N, D, seed=130000 + case, dtype=dtype)
+        head = [(int(rng.integers(0, B)), int(rng.integers(0, H)))]
+        for one_pass in (True, False):
+            check_heads(q, k, v, g, causal, _scale(D), heads=head, label=f"sweep{case}",
+                        one_pass=one_pass)
