@@ -929,9 +929,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_fused_kernel(
   // a workgroup with a later ticket, so all key workgroups of a head must be
   // resident together: at most one per CU of an XCD. A wait in the
   // middle of step n is for a counter passed in the middle of step
-  // n + 1 - rot of another workgroup: rot = 2 keeps every wait behind an
-  // earlier event (rot = 1 would allow a cycle of waits), and rot = 0 only
-  // waits for lower key tiles.
+  // n + 1 - rot of another workgroup, and a pass needs nothing but the
+  // passing workgroup's barrier at the end of the step before, so every
+  // chain of waits runs back through earlier steps and none closes into a
+  // cycle (rot = 1 as well, which measured no faster than 2; rot = 0 only
+  // waits for lower key tiles).
   const int rot = tiles_n <= cus_per_xcc && t_end >= 2 * tiles_n ? 2 : 0;
   auto tile_at = [&](int n) {  // query tile of step n
     const int t = n - jk * rot;
